@@ -1,0 +1,238 @@
+"""Python binding of libsolattn: MI355X (gfx950) query-thresholded block-sparse
+attention with a Taylor term for rejected blocks (Sol-Attn style).
+
+This module only marshals arguments: it checks shapes and dtypes, allocates
+output tensors with torch, and calls the C ABI (``include/solattn.h``) on the
+current HIP stream.  Every step of the computation runs in the HIP kernels of
+``libsolattn.so``; there is no CPU or PyTorch fallback.  If the library is not
+built, every call raises.
+
+Tensors are torch tensors on the GPU, ``[H, N, 128]`` contiguous, bf16 for
+q/k/v/out, fp32 for the rest.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "SOL_DENSE",
+    "SOL_SPARSE",
+    "SolAttnError",
+    "library_path",
+    "load_library",
+    "sol_attn_pool",
+    "sol_attn_row_stats",
+    "sol_attn_forward",
+    "sol_attn_workspace_size",
+    "attn_lse_merge",
+    "sol_attn_error_string",
+    "sol_attn_proxy_scores",
+    "sol_attn_block_mask",
+]
+
+SOL_DENSE = 0
+SOL_SPARSE = 1
+HEAD_DIM = 128
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libsolattn.so"
+_lib = None
+
+
+class SolAttnError(RuntimeError):
+    """A negative return code from the C ABI."""
+
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed with code {code}: {sol_attn_error_string(code)}")
+        self.code = code
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libsolattn.so from the package directory (built by ``build.py``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m block_sparse_attention_06_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    P, I, F, S, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_char_p
+    sigs = {
+        "sol_attn_pool": (I, [P, P, P, P, I, I, I, I, P]),
+        "sol_attn_row_stats": (I, [P, P, P, P, I, I, I, I, I, P]),
+        "sol_attn_forward": (I, [P, P, P, P, P, I, I, I, I, F, I, I, P, S, P]),
+        "sol_attn_workspace_size": (S, [I, I, I, I, I, I]),
+        "attn_lse_merge": (I, [P, P, P, P, P, P, I, I, I, P]),
+        "sol_attn_error_string": (Z, [I]),
+        "sol_attn_proxy_scores": (I, [P, P, P, I, I, I, I, I, I, I, P]),
+        "sol_attn_block_mask": (I, [P, P, P, P, F, I, I, I, I, I, I, I, P, P, P]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def sol_attn_error_string(code: int) -> str:
+    return load_library().sol_attn_error_string(int(code)).decode()
+
+
+def _check(fn: str, code: int) -> None:
+    if code != 0:
+        raise SolAttnError(fn, code)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _want(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+def sol_attn_pool(k: torch.Tensor, v: torch.Tensor, B: int, stream=None):
+    """Block means ``(kbar, vbar)`` ``[H, ceil(N/B), 128]`` fp32 of keys and values."""
+    lib = load_library()
+    _want(k, "k", torch.bfloat16, 3)
+    _want(v, "v", torch.bfloat16, 3)
+    H, N, d = k.shape
+    nb = (N + B - 1) // B
+    kbar = torch.empty((H, nb, d), dtype=torch.float32, device=k.device)
+    vbar = torch.empty_like(kbar)
+    _check("sol_attn_pool", lib.sol_attn_pool(_ptr(k), _ptr(v), _ptr(kbar), _ptr(vbar),
+                                              N, H, d, int(B), _stream(stream)))
+    return kbar, vbar
+
+
+def sol_attn_row_stats(q: torch.Tensor, kbar: torch.Tensor, B: int, Nk: int, stream=None):
+    """``(mu, sigma)`` ``[H, N]`` fp32 of the block proxy scores of every query row."""
+    lib = load_library()
+    _want(q, "q", torch.bfloat16, 3)
+    _want(kbar, "kbar", torch.float32, 3)
+    H, N, d = q.shape
+    mu = torch.empty((H, N), dtype=torch.float32, device=q.device)
+    sigma = torch.empty_like(mu)
+    _check("sol_attn_row_stats", lib.sol_attn_row_stats(
+        _ptr(q), _ptr(kbar), _ptr(mu), _ptr(sigma), N, int(Nk), H, d, int(B), _stream(stream)))
+    return mu, sigma
+
+
+def sol_attn_workspace_size(N: int, Nk: int, H: int, d: int, B: int, mode: int) -> int:
+    return int(load_library().sol_attn_workspace_size(N, Nk, H, d, B, mode))
+
+
+def sol_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, B: int = 128,
+                     beta: float = 0.5, mode: int = SOL_SPARSE,
+                     workspace: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     want_lse: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention forward; returns ``(out [H,N,128] bf16, lse [H,N] fp32 or None)``.
+
+    ``workspace`` (uint8, at least ``sol_attn_workspace_size`` bytes) is allocated
+    when not given; pass one to keep the call free of allocations."""
+    lib = load_library()
+    _want(q, "q", torch.bfloat16, 3)
+    _want(k, "k", torch.bfloat16, 3)
+    _want(v, "v", torch.bfloat16, 3)
+    H, N, d = q.shape
+    Nk = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != H or k.shape[2] != d:
+        raise ValueError("k and v must be [H, Nk, d] with q's H and d")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _want(out, "out", torch.bfloat16, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if lse is None and want_lse:
+        lse = torch.empty((H, N), dtype=torch.float32, device=q.device)
+    ws_bytes = sol_attn_workspace_size(N, Nk, H, d, B, mode)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if math.isnan(beta):
+        raise ValueError("beta must not be NaN")
+    _check("sol_attn_forward", lib.sol_attn_forward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), N, H, d, int(B), float(beta),
+        int(mode), Nk, _ptr(workspace), have, _stream(stream)))
+    return out, lse
+
+
+def attn_lse_merge(out_a: torch.Tensor, lse_a: torch.Tensor, out_b: torch.Tensor,
+                   lse_b: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, stream=None):
+    """Exact merge of two partial answers over disjoint keys; returns ``(out, lse)``."""
+    lib = load_library()
+    for t, n in ((out_a, "out_a"), (out_b, "out_b")):
+        _want(t, n, torch.bfloat16, 3)
+    for t, n in ((lse_a, "lse_a"), (lse_b, "lse_b")):
+        _want(t, n, torch.float32, 2)
+    H, N, d = out_a.shape
+    if out is None:
+        out = torch.empty_like(out_a)
+    if lse is None:
+        lse = torch.empty_like(lse_a)
+    _check("attn_lse_merge", lib.attn_lse_merge(
+        _ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), _ptr(out), _ptr(lse), N, H, d,
+        _stream(stream)))
+    return out, lse
+
+
+def sol_attn_proxy_scores(q: torch.Tensor, kbar: torch.Tensor, B: int, Nk: int,
+                          row0: int = 0, nrows: Optional[int] = None, stream=None):
+    """Proxy scores ``[H, nrows, nb]`` fp32 as the forward kernel computes them."""
+    lib = load_library()
+    _want(q, "q", torch.bfloat16, 3)
+    _want(kbar, "kbar", torch.float32, 3)
+    H, N, d = q.shape
+    nrows = N - row0 if nrows is None else nrows
+    nb = (Nk + B - 1) // B
+    p = torch.empty((H, nrows, nb), dtype=torch.float32, device=q.device)
+    _check("sol_attn_proxy_scores", lib.sol_attn_proxy_scores(
+        _ptr(q), _ptr(kbar), _ptr(p), int(row0), int(nrows), N, int(Nk), H, d, int(B),
+        _stream(stream)))
+    return p
+
+
+def sol_attn_block_mask(q: torch.Tensor, kbar: torch.Tensor, mu: torch.Tensor,
+                        sigma: torch.Tensor, beta: float, B: int, Nk: int, row0: int = 0,
+                        nrows: Optional[int] = None, want_mask: bool = True, stream=None):
+    """Selection mask ``[H, nrows, nb]`` uint8 (or None) and the four density counts
+    (selected pairs, 32-row tile pairs, 128-row tile pairs, 128-row tile total)."""
+    lib = load_library()
+    _want(q, "q", torch.bfloat16, 3)
+    _want(kbar, "kbar", torch.float32, 3)
+    H, N, d = q.shape
+    nrows = N - row0 if nrows is None else nrows
+    nb = (Nk + B - 1) // B
+    mask = torch.empty((H, nrows, nb), dtype=torch.uint8, device=q.device) if want_mask else None
+    counts = torch.empty(4, dtype=torch.int64, device=q.device)
+    _check("sol_attn_block_mask", lib.sol_attn_block_mask(
+        _ptr(q), _ptr(kbar), _ptr(mu), _ptr(sigma), float(beta), int(row0), int(nrows), N,
+        int(Nk), H, d, int(B), _ptr(mask), _ptr(counts), _stream(stream)))
+    return mask, counts

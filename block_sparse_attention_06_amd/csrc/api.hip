@@ -1,0 +1,228 @@
+// C ABI of libsolattn (declared in include/solattn.h): argument checks,
+// workspace layout, split planning and kernel launches on the caller's stream.
+// Nothing here allocates, frees or synchronises.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/solattn.h"
+#include "launch.hpp"
+
+using namespace solattn;
+
+namespace {
+
+constexpr int kCUs = 256;            // MI355X compute units
+constexpr int kSplitTarget = 4 * kCUs;  // workgroups wanted before splitting keys stops
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+struct Split {
+  int nb, nb_pad, splits, tiles_per_split;
+};
+
+// Short query sets leave most CUs idle (one workgroup per 128 rows per head);
+// then the key tiles are split over workgroups (doubleAI page, "Attention
+// across two GPUs": split the work along the keys) and merged afterwards.
+Split plan_split(int N, int Nk, int H, int KB, bool sparse) {
+  Split p{};
+  p.nb = cdiv(Nk, KB);
+  p.nb_pad = (int)round_up((size_t)p.nb, 32);
+  const long long wgs = (long long)H * cdiv(N, 128);
+  p.splits = 1;
+  p.tiles_per_split = p.nb;
+  if (wgs < 2 * kCUs) {
+    int target = (int)((kSplitTarget + wgs - 1) / wgs);
+    if (target > p.nb) target = p.nb;
+    int tps = cdiv(p.nb, target);
+    if (sparse) tps = (int)round_up((size_t)tps, 32);  // routing chunks stay aligned
+    p.tiles_per_split = tps;
+    p.splits = cdiv(p.nb, tps);
+  }
+  return p;
+}
+
+struct Plan {
+  Split sp, dn;  // sparse plan (blocks of B) and dense plan (tiles of 128 keys)
+  int max_splits;
+  size_t off_kbar, off_vbar, off_vsum, off_mu, off_sigma, off_po, off_pml, bytes;
+};
+
+// Sizes are validated by the caller.  A sparse-mode workspace also covers the
+// dense kernel, which runs when beta = -inf.
+Plan make_plan(int N, int Nk, int H, int B, int mode) {
+  Plan p{};
+  const bool sparse = mode == SOL_SPARSE;
+  p.dn = plan_split(N, Nk, H, 128, false);
+  p.max_splits = p.dn.splits;
+  if (sparse) {
+    p.sp = plan_split(N, Nk, H, B, true);
+    if (p.sp.splits > p.max_splits) p.max_splits = p.sp.splits;
+  }
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  const size_t HN = (size_t)H * N;
+  if (sparse) {
+    p.off_kbar = take((size_t)H * p.sp.nb * 128 * sizeof(float));
+    p.off_vbar = take((size_t)H * p.sp.nb * 128 * sizeof(float));
+    p.off_vsum = take((size_t)H * 128 * p.sp.nb_pad * sizeof(uint16_t));
+    p.off_mu = take(HN * sizeof(float));
+    p.off_sigma = take(HN * sizeof(float));
+  }
+  if (p.max_splits > 1) {
+    p.off_po = take((size_t)p.max_splits * HN * 128 * sizeof(float));
+    p.off_pml = take((size_t)p.max_splits * HN * 2 * sizeof(float));
+  }
+  p.bytes = off;
+  return p;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SOL_OK : SOL_ERR_HIP; }
+
+int check_shape(int N, int H, int d) {
+  if (N <= 0 || H <= 0) return SOL_ERR_INVALID_ARG;
+  if (d != 128) return SOL_ERR_UNSUPPORTED;
+  return SOL_OK;
+}
+
+int check_block(int B) { return (B == 64 || B == 128) ? SOL_OK : SOL_ERR_UNSUPPORTED; }
+
+}  // namespace
+
+extern "C" {
+
+const char* sol_attn_error_string(int code) {
+  switch (code) {
+    case SOL_OK: return "ok";
+    case SOL_ERR_INVALID_ARG: return "invalid argument (null pointer, size, NaN beta, workspace or alignment)";
+    case SOL_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 128, block 64 or 128, mode 0 or 1)";
+    case SOL_ERR_HIP: return "HIP runtime reported a launch error";
+    default: return "unknown error code";
+  }
+}
+
+int sol_attn_pool(const uint16_t* k, const uint16_t* v, float* kbar, float* vbar, int N, int H,
+                  int d, int B, void* stream) {
+  if (!k || !v || !kbar || !vbar) return SOL_ERR_INVALID_ARG;
+  if (int r = check_shape(N, H, d)) return r;
+  if (int r = check_block(B)) return r;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(kbar, 16) || !aligned(vbar, 16))
+    return SOL_ERR_INVALID_ARG;
+  PoolArgs a{k, v, kbar, vbar, nullptr, N, H, B, cdiv(N, B), 0};
+  return hip_status(launch_pool(a, (hipStream_t)stream));
+}
+
+int sol_attn_row_stats(const uint16_t* q, const float* kbar, float* mu, float* sigma, int N,
+                       int Nk, int H, int d, int B, void* stream) {
+  if (!q || !kbar || !mu || !sigma) return SOL_ERR_INVALID_ARG;
+  if (Nk == 0) Nk = N;
+  if (Nk < 0) return SOL_ERR_INVALID_ARG;
+  if (int r = check_shape(N, H, d)) return r;
+  if (int r = check_block(B)) return r;
+  if (!aligned(q, 16) || !aligned(kbar, 16)) return SOL_ERR_INVALID_ARG;
+  StatsArgs a{q, kbar, mu, sigma, N, H, cdiv(Nk, B)};
+  return hip_status(launch_stats(a, (hipStream_t)stream));
+}
+
+size_t sol_attn_workspace_size(int N, int Nk, int H, int d, int B, int mode) {
+  if (Nk == 0) Nk = N;
+  if (N <= 0 || Nk <= 0 || H <= 0 || d != 128) return 0;
+  if (mode != SOL_DENSE && mode != SOL_SPARSE) return 0;
+  if (mode == SOL_SPARSE && check_block(B)) return 0;
+  return make_plan(N, Nk, H, B, mode).bytes;
+}
+
+int sol_attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                     float* lse, int N, int H, int d, int B, float beta, int mode, int Nk,
+                     void* workspace, size_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !out) return SOL_ERR_INVALID_ARG;
+  if (Nk == 0) Nk = N;
+  if (Nk < 0) return SOL_ERR_INVALID_ARG;
+  if (int r = check_shape(N, H, d)) return r;
+  if (mode != SOL_DENSE && mode != SOL_SPARSE) return SOL_ERR_UNSUPPORTED;
+  if (mode == SOL_SPARSE) {
+    if (int r = check_block(B)) return r;
+    if (isnan(beta)) return SOL_ERR_INVALID_ARG;
+  }
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return SOL_ERR_INVALID_ARG;
+  const Plan p = make_plan(N, Nk, H, B, mode);
+  if (p.bytes > 0 && (!workspace || ws_bytes < p.bytes || !aligned(workspace, 256)))
+    return SOL_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const bool sparse = mode == SOL_SPARSE && !(isinf(beta) && beta < 0);
+  const Split& sp = sparse ? p.sp : p.dn;
+
+  FwdArgs f{};
+  f.q = q; f.k = k; f.v = v; f.out = out; f.lse = lse;
+  f.beta = beta; f.N = N; f.Nk = Nk; f.H = H;
+  f.nb = sp.nb; f.nb_pad = sp.nb_pad;
+  f.n_qt = cdiv(N, 128);
+  f.splits = sp.splits; f.tiles_per_split = sp.tiles_per_split;
+  f.total = H * f.n_qt * f.splits;
+  if (sparse) {
+    PoolArgs pa{k, v, (float*)(ws + p.off_kbar), (float*)(ws + p.off_vbar),
+                (uint16_t*)(ws + p.off_vsum), Nk, H, B, sp.nb, sp.nb_pad};
+    if (int r = hip_status(launch_pool(pa, s))) return r;
+    StatsArgs sa{q, pa.kbar, (float*)(ws + p.off_mu), (float*)(ws + p.off_sigma), N, H, sp.nb};
+    if (int r = hip_status(launch_stats(sa, s))) return r;
+    f.kbar = pa.kbar; f.vsumT = pa.vsumT; f.mu = sa.mu; f.sigma = sa.sigma;
+  }
+  if (f.splits > 1) {
+    f.part_o = (float*)(ws + p.off_po);
+    f.part_ml = (float*)(ws + p.off_pml);
+  }
+  if (int r = hip_status(launch_forward(f, sparse, sparse ? B : 128, s))) return r;
+  if (f.splits > 1) {
+    CombineArgs c{f.part_o, f.part_ml, out, lse, N, H, f.splits};
+    if (int r = hip_status(launch_combine(c, s))) return r;
+  }
+  return SOL_OK;
+}
+
+int attn_lse_merge(const uint16_t* out_a, const float* lse_a, const uint16_t* out_b,
+                   const float* lse_b, uint16_t* out, float* lse, int N, int H, int d,
+                   void* stream) {
+  if (!out_a || !lse_a || !out_b || !lse_b || !out || !lse) return SOL_ERR_INVALID_ARG;
+  if (int r = check_shape(N, H, d)) return r;
+  if (!aligned(out_a, 16) || !aligned(out_b, 16) || !aligned(out, 16)) return SOL_ERR_INVALID_ARG;
+  MergeArgs a{out_a, lse_a, out_b, lse_b, out, lse, N, H};
+  return hip_status(launch_merge(a, (hipStream_t)stream));
+}
+
+int sol_attn_proxy_scores(const uint16_t* q, const float* kbar, float* p, int row0, int nrows,
+                          int N, int Nk, int H, int d, int B, void* stream) {
+  if (!q || !kbar || !p) return SOL_ERR_INVALID_ARG;
+  if (Nk == 0) Nk = N;
+  if (Nk < 0 || row0 < 0 || nrows <= 0 || row0 + nrows > N) return SOL_ERR_INVALID_ARG;
+  if (int r = check_shape(N, H, d)) return r;
+  if (int r = check_block(B)) return r;
+  if (!aligned(q, 16) || !aligned(kbar, 16)) return SOL_ERR_INVALID_ARG;
+  ProxyArgs a{q, kbar, p, row0, nrows, N, H, cdiv(Nk, B)};
+  return hip_status(launch_proxy(a, (hipStream_t)stream));
+}
+
+int sol_attn_block_mask(const uint16_t* q, const float* kbar, const float* mu, const float* sigma,
+                        float beta, int row0, int nrows, int N, int Nk, int H, int d, int B,
+                        uint8_t* mask, int64_t* counts, void* stream) {
+  if (!q || !kbar || !mu || !sigma || !counts) return SOL_ERR_INVALID_ARG;
+  if (Nk == 0) Nk = N;
+  if (Nk < 0 || row0 < 0 || nrows <= 0 || row0 + nrows > N || (row0 % 128) != 0)
+    return SOL_ERR_INVALID_ARG;
+  if (isnan(beta)) return SOL_ERR_INVALID_ARG;
+  if (int r = check_shape(N, H, d)) return r;
+  if (int r = check_block(B)) return r;
+  if (!aligned(q, 16) || !aligned(kbar, 16) || !aligned(counts, 8)) return SOL_ERR_INVALID_ARG;
+  MaskArgs a{q, kbar, mu, sigma, beta, mask, (unsigned long long*)counts, row0, nrows, N, H,
+             cdiv(Nk, B)};
+  return hip_status(launch_mask(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// Device-side building blocks shared by the gfx950 kernels of libsolattn.
+//
+// Wave64 MFMA conventions used throughout (checked on gfx950):
+//   v_mfma_f32_32x32x16_bf16, D[32x32] += A[32x16] * B[16x32]:
+//     lane l supplies A row (l % 32), k = 8*(l / 32) .. +8 and
+//                     B col (l % 32), k = 8*(l / 32) .. +8;
+//     lane l holds    D col (l % 32), rows 8*(i/4) + 4*(l/32) + (i%4), i < 16.
+// Every attention product is computed transposed (S^T = K Q^T, O^T = V^T P^T),
+// so that each lane owns one query row (column l % 32) and all of that row's
+// accumulators: row maxima, rescaling and Taylor weights need no shuffles
+// beyond one exchange with the partner lane l ^ 32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace solattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16;
+
+constexpr int kHeadDim = 128;
+constexpr int kChunk = 32;       // key blocks routed together (one MFMA tile of blocks)
+constexpr int kQTile = 128;      // query rows per workgroup (4 waves x 32)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ float bf16_to_f32(u16 b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest even (finite inputs).
+__device__ __forceinline__ u16 f32_to_bf16_bits(float x) {
+  return __builtin_bit_cast(u16, (__bf16)x);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Position of block/key k (0..15) inside its group of 16 in the permuted
+// "k-major" layouts: lane half g of an MFMA operand reads positions 8g..8g+7,
+// which hold keys {4g..4g+3, 8+4g..8+4g+3} -- the keys that lane half holds in
+// the accumulator layout above.
+__device__ __forceinline__ int perm16(int k) { return ((k & 7) >> 2) * 8 + (k >> 3) * 4 + (k & 3); }
+
+// Offset, inside a 32-wide accumulator tile, of element i held by lane half g.
+__device__ __forceinline__ int acc_row(int i, int g) { return (i >> 2) * 8 + g * 4 + (i & 3); }
+
+// Query fragment of one wave: lane l holds row (l % 32) of the wave's 32 rows,
+// k-step ks covers dims 16 ks + 8 (l/32) .. +8.
+struct QFrag {
+  bf16x8 k[8];
+};
+
+__device__ __forceinline__ void load_qfrag(QFrag& qf, const u16* qhead, int row, bool valid, int g) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(qhead + (int64_t)row * kHeadDim);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (valid) x = p[ks * 2 + g];
+    qf.k[ks] = as_bf16x8(x);
+  }
+}
+
+// Proxy scores p = (q . kbar_j) / sqrt(d) of the wave's 32 rows against the 32
+// pooled keys b0 .. b0+31 (Sol-Engine LTX25 page, "Stage 2 Optimization --
+// Core Technology: Sol-Attn": block proxy scores from pooled keys).
+// kbar is fp32; it enters the bf16 MFMA as hi + lo bf16 parts (q is exact in
+// bf16), so p carries ~16 significant bits of kbar instead of 8.
+// Result element i of lane l: block b0 + acc_row(i, l/32), query row l % 32.
+// Blocks >= nb read a clamped row; callers ignore those elements.
+// Every kernel that routes uses this one function, so the proxy scores the
+// inspection exports report are the ones the forward kernel compares.
+__device__ __forceinline__ f32x16 proxy_chunk(const QFrag& qf, const float* kbar_head, int b0,
+                                              int nb, int lane) {
+  const int g = lane >> 5;
+  int blk = b0 + (lane & 31);
+  blk = blk < nb ? blk : nb - 1;
+  const f32x4* row = reinterpret_cast<const f32x4*>(kbar_head + (int64_t)blk * kHeadDim);
+  f32x16 acc = {};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    f32x4 x0 = row[ks * 4 + g * 2];
+    f32x4 x1 = row[ks * 4 + g * 2 + 1];
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      __bf16 h0 = (__bf16)x0[e];
+      __bf16 h1 = (__bf16)x1[e];
+      hi[e] = h0;
+      hi[e + 4] = h1;
+      lo[e] = (__bf16)(x0[e] - (float)h0);
+      lo[e + 4] = (__bf16)(x1[e] - (float)h1);
+    }
+    acc = mfma32(hi, qf.k[ks], acc);
+    acc = mfma32(lo, qf.k[ks], acc);
+  }
+  const float scale = 0.08838834764831845f;  // 1/sqrt(128)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] *= scale;
+  return acc;
+}
+
+// Row threshold tau = mu + beta sigma (Sol-Engine LTX25 page, bullet
+// "Query-dependent thresholding").  beta = +inf selects nothing.
+__device__ __forceinline__ float make_tau(float mu, float sigma, float beta) {
+  if (__builtin_isinf(beta)) return beta > 0.f ? __builtin_inff() : -__builtin_inff();
+  return __builtin_fmaf(beta, sigma, mu);
+}
+
+// A block is attended exactly when its proxy is at or above the threshold.
+__device__ __forceinline__ bool is_selected(float p, float tau) { return p >= tau; }
+
+}  // namespace solattn

@@ -1,0 +1,90 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace solattn {
+
+struct PoolArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  float* kbar;      // [H, nb, 128]
+  float* vbar;      // [H, nb, 128]
+  uint16_t* vsumT;  // [H, 128, nb_pad] bf16 block sums, permuted groups of 16; may be null
+  int N, H, B, nb, nb_pad;
+};
+
+struct StatsArgs {
+  const uint16_t* q;
+  const float* kbar;
+  float* mu;
+  float* sigma;
+  int N, H, nb;
+};
+
+struct ProxyArgs {
+  const uint16_t* q;
+  const float* kbar;
+  float* p;  // [H, nrows, nb]
+  int row0, nrows, N, H, nb;
+};
+
+struct MaskArgs {
+  const uint16_t* q;
+  const float* kbar;
+  const float* mu;
+  const float* sigma;
+  float beta;
+  uint8_t* mask;  // [H, nrows, nb] or null
+  unsigned long long* counts;  // [4]
+  int row0, nrows, N, H, nb;
+};
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  float* lse;          // may be null
+  const float* kbar;   // sparse only
+  const uint16_t* vsumT;
+  const float* mu;
+  const float* sigma;
+  float* part_o;       // [S, H, N, 128] when S > 1
+  float* part_ml;      // [S, H, N, 2]   (max in log2 units, denominator)
+  float beta;
+  int N, Nk, H;
+  int nb, nb_pad;      // key tiles (sparse: blocks of B) and padded count
+  int n_qt;            // query tiles of 128 rows
+  int splits, tiles_per_split;
+  int total;           // H * n_qt * splits
+};
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_ml;
+  uint16_t* out;
+  float* lse;
+  int N, H, splits;
+};
+
+struct MergeArgs {
+  const uint16_t* out_a;
+  const float* lse_a;
+  const uint16_t* out_b;
+  const float* lse_b;
+  uint16_t* out;
+  float* lse;
+  int N, H;
+};
+
+hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
+hipError_t launch_stats(const StatsArgs& a, hipStream_t s);
+hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s);
+hipError_t launch_mask(const MaskArgs& a, hipStream_t s);
+hipError_t launch_forward(const FwdArgs& a, bool sparse, int B, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+}  // namespace solattn

@@ -1,0 +1,220 @@
+// Routing kernels: block mean-pool, proxy-score row statistics, and the two
+// inspection kernels (proxy scores of a row range, block selection mask).
+//
+// Sol-Engine LTX25 page, "Stage 2 Optimization -- Core Technology: Sol-Attn":
+// pooled keys give per-row block proxy scores whose mean and spread set the
+// row's threshold.  All of this is HBM- or L2-bound; nothing here stores the
+// proxy map of a full sequence.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace solattn {
+
+// ---------------------------------------------------------------------------
+// Block mean-pool.  One workgroup per (key block j, head h, tensor K|V).
+// 256 threads = 16 row groups x 16 column chunks of 8 bf16 (16 B): every load
+// instruction of a wave reads 4 whole 256-byte rows (coalesced), and each
+// thread keeps all its row loads in flight before summing.
+// For V the block sum is also written, transposed and permuted, as bf16 for
+// the Taylor MFMA of the forward kernel.
+// ---------------------------------------------------------------------------
+template <int B>
+__global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
+  __shared__ float part[16][kHeadDim + 4];
+  const int j = blockIdx.x, h = blockIdx.y, which = blockIdx.z;
+  const int tid = threadIdx.x, chunk = tid & 15, rg = tid >> 4;
+  if (j >= a.nb) {  // zero padding of the transposed block sums
+    if (which == 1 && a.vsumT && tid < kHeadDim) {
+      int pj = (j & ~15) + perm16(j & 15);
+      a.vsumT[((int64_t)h * kHeadDim + tid) * a.nb_pad + pj] = 0;
+    }
+    return;
+  }
+  const uint16_t* src = (which ? a.v : a.k) + ((int64_t)h * a.N + (int64_t)j * B) * kHeadDim;
+  const int n = min(B, a.N - j * B);
+  constexpr int R = B / 16;
+  u32x4 x[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int t = rg + 16 * r;
+    x[r] = t < n ? *reinterpret_cast<const u32x4*>(src + (int64_t)t * kHeadDim + chunk * 8)
+                 : u32x4{0u, 0u, 0u, 0u};
+  }
+  float acc[8] = {};
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += __uint_as_float(x[r][e] << 16);
+      acc[2 * e + 1] += __uint_as_float(x[r][e] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[rg][chunk * 8 + e] = acc[e];
+  __syncthreads();
+  if (tid < kHeadDim) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += part[r][tid];
+    float mean = s / (float)n;
+    float* dst = which ? a.vbar : a.kbar;
+    dst[((int64_t)h * a.nb + j) * kHeadDim + tid] = mean;
+    if (which == 1 && a.vsumT) {
+      int pj = (j & ~15) + perm16(j & 15);
+      a.vsumT[((int64_t)h * kHeadDim + tid) * a.nb_pad + pj] = f32_to_bf16_bits(s);
+    }
+  }
+}
+
+hipError_t launch_pool(const PoolArgs& a, hipStream_t s) {
+  dim3 grid(a.vsumT ? a.nb_pad : a.nb, a.H, 2);
+  if (a.B == 64)
+    pool_kernel<64><<<grid, 256, 0, s>>>(a);
+  else
+    pool_kernel<128><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Row statistics mu_i, sigma_i of p_i. over all key blocks.  One wave per 32
+// query rows, four waves per workgroup.  Proxy tiles come from proxy_chunk;
+// the sums are shifted by the row's first proxy p_i0 so the variance has no
+// cancellation, then reduced over the two lane halves.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
+  const int h = blockIdx.y;
+  const int row = blockIdx.x * kQTile + wave * 32 + (lane & 31);
+  const bool valid = row < a.N;
+  QFrag qf;
+  load_qfrag(qf, a.q + (int64_t)h * a.N * kHeadDim, row, valid, g);
+  const float* kb = a.kbar + (int64_t)h * a.nb * kHeadDim;
+  float shift = 0.f, s1 = 0.f, s2 = 0.f;
+  for (int b0 = 0; b0 < a.nb; b0 += kChunk) {
+    f32x16 p = proxy_chunk(qf, kb, b0, a.nb, lane);
+    if (b0 == 0) shift = __shfl(p[0], lane & 31);  // block 0 sits in element 0 of lane half 0
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (b0 + acc_row(i, g) < a.nb) {
+        float x = p[i] - shift;
+        s1 += x;
+        s2 = __builtin_fmaf(x, x, s2);
+      }
+    }
+  }
+  s1 += __shfl_xor(s1, 32);
+  s2 += __shfl_xor(s2, 32);
+  if (g == 0 && valid) {
+    float inv = 1.f / (float)a.nb;
+    float md = s1 * inv;
+    float var = __builtin_fmaf(-md, md, s2 * inv);
+    a.mu[(int64_t)h * a.N + row] = shift + md;
+    a.sigma[(int64_t)h * a.N + row] = sqrtf(fmaxf(var, 0.f));
+  }
+}
+
+hipError_t launch_stats(const StatsArgs& a, hipStream_t s) {
+  dim3 grid((a.N + kQTile - 1) / kQTile, a.H);
+  stats_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Inspection: proxy scores of a row range.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void proxy_kernel(ProxyArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
+  const int h = blockIdx.y;
+  const int rl = blockIdx.x * kQTile + wave * 32 + (lane & 31);  // local row
+  const int row = a.row0 + rl;
+  const bool valid = rl < a.nrows && row < a.N;
+  QFrag qf;
+  load_qfrag(qf, a.q + (int64_t)h * a.N * kHeadDim, row, valid, g);
+  const float* kb = a.kbar + (int64_t)h * a.nb * kHeadDim;
+  for (int b0 = 0; b0 < a.nb; b0 += kChunk) {
+    f32x16 p = proxy_chunk(qf, kb, b0, a.nb, lane);
+    if (!valid) continue;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int blk = b0 + acc_row(i, g);
+      if (blk < a.nb) a.p[((int64_t)h * a.nrows + rl) * a.nb + blk] = p[i];
+    }
+  }
+}
+
+hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s) {
+  dim3 grid((a.nrows + kQTile - 1) / kQTile, a.H);
+  proxy_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Inspection: selection mask and density counts, with the forward kernel's
+// predicate (same proxy_chunk, make_tau and is_selected).
+// ---------------------------------------------------------------------------
+__global__ void zero_counts_kernel(unsigned long long* c) {
+  if (threadIdx.x < 4) c[threadIdx.x] = 0ull;
+}
+
+__global__ __launch_bounds__(256) void mask_kernel(MaskArgs a) {
+  __shared__ uint32_t wmask[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
+  const int h = blockIdx.y;
+  const int rl = blockIdx.x * kQTile + wave * 32 + (lane & 31);
+  const int row = a.row0 + rl;
+  const bool valid = rl < a.nrows && row < a.N;
+  QFrag qf;
+  load_qfrag(qf, a.q + (int64_t)h * a.N * kHeadDim, row, valid, g);
+  const float* kb = a.kbar + (int64_t)h * a.nb * kHeadDim;
+  float tau = __builtin_inff();
+  if (valid) tau = make_tau(a.mu[(int64_t)h * a.N + row], a.sigma[(int64_t)h * a.N + row], a.beta);
+  unsigned long long n_sel = 0, n_t32 = 0, n_t128 = 0, n_pairs = 0;
+  for (int b0 = 0; b0 < a.nb; b0 += kChunk) {
+    f32x16 p = proxy_chunk(qf, kb, b0, a.nb, lane);
+    uint32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int off = acc_row(i, g);
+      int blk = b0 + off;
+      bool sel = valid && blk < a.nb && is_selected(p[i], tau);
+      mine |= (uint32_t)sel << off;
+      if (valid && blk < a.nb && a.mask)
+        a.mask[((int64_t)h * a.nrows + rl) * a.nb + blk] = sel ? 1 : 0;
+    }
+    n_sel += __popc(mine);
+    uint32_t wu = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) wu |= __shfl_xor(wu, o);
+    __syncthreads();
+    if (lane == 0) wmask[wave] = wu;
+    __syncthreads();
+    if (lane == 0) {
+      n_t32 += __popc(wu);
+      if (wave == 0) {
+        uint32_t u = wmask[0] | wmask[1] | wmask[2] | wmask[3];
+        n_t128 += __popc(u);
+        n_pairs += min(kChunk, a.nb - b0);
+      }
+    }
+  }
+  // per-lane selected counts -> wave sum
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) n_sel += __shfl_xor(n_sel, o);
+  if (lane == 0) {
+    atomicAdd(&a.counts[0], n_sel);
+    atomicAdd(&a.counts[1], n_t32);
+    if (wave == 0) {
+      atomicAdd(&a.counts[2], n_t128);
+      atomicAdd(&a.counts[3], n_pairs);
+    }
+  }
+}
+
+hipError_t launch_mask(const MaskArgs& a, hipStream_t s) {
+  zero_counts_kernel<<<1, 64, 0, s>>>(a.counts);
+  dim3 grid((a.nrows + kQTile - 1) / kQTile, a.H);
+  mask_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace solattn

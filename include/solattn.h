@@ -1,0 +1,170 @@
+/*
+ * solattn.h -- C ABI of the MI355X (gfx950) query-thresholded block-sparse
+ * attention library (libsolattn.so).
+ *
+ * The operation (Sol-Attn style, training-free):
+ *   "Accelerating LTX-2.5 with Sol Engine" (NVlabs Sana Sol-Engine/LTX25 page),
+ *   section "Stage 2 Optimization -- Core Technology: Sol-Attn":
+ *     - each query row i derives a threshold tau_i = mu_i + beta * sigma_i from
+ *       the statistics of its block proxy scores (bullet "Query-dependent
+ *       thresholding");
+ *     - pooled keys are streamed chunk-wise and compared with the threshold
+ *       inside the online-softmax pass, with no proxy map stored (bullet
+ *       "On-the-fly routing");
+ *     - rejected blocks are approximated by a Taylor expansion about the
+ *       row-wise mean score (bullet "Proxy-score reuse").
+ *   The pages give the Taylor term only in words.  This library fixes it as:
+ *   a rejected key block j (n_j valid tokens, mean key kbar_j, mean value
+ *   vbar_j) contributes weight w_ij = n_j * e^{mu_i} * (1 + p_ij - mu_i) on
+ *   vbar_j to the numerator and w_ij to the denominator, where
+ *   p_ij = q_i . kbar_j / sqrt(d) and mu_i, sigma_i are the mean and the
+ *   population standard deviation of p_i. over all key blocks.  Selected
+ *   blocks (p_ij >= tau_i) are attended exactly.  beta = -inf is plain dense
+ *   softmax attention.
+ *
+ *   "LTX-2.5 at 4K, in half the time" (doubleAI page), section "Attention
+ *   across two GPUs": partial answers over disjoint key sets carry their
+ *   log-sum-exp and merge exactly (attn_lse_merge); the work of a short query
+ *   is split along the keys (done inside sol_attn_forward); a ragged key count
+ *   is handled by dropping, never padding, the missing keys.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are row-major, contiguous, [H, rows, d]; batch folds into H.
+ *     bf16 tensors are passed as uint16_t bit patterns.
+ *   - All pointers are device pointers (HIP device memory) unless stated.
+ *     The caller owns every buffer.  Inputs are only read; outputs are
+ *     written in full.  The library never allocates, frees or synchronises:
+ *     all work is enqueued on `stream` (a hipStream_t; NULL = null stream).
+ *   - Softmax scale is 1/sqrt(d).  Only d = 128 is supported; B is 64 or 128.
+ *   - Return codes: SOL_OK, or a negative SOL_ERR_*.  Arguments are checked
+ *     before anything is enqueued; on an error nothing is launched.
+ *     SOL_ERR_HIP reports a launch failure from the HIP runtime.
+ *   - Stateless and thread-safe.  Calls on different streams that write
+ *     disjoint outputs may overlap.
+ *   - Offsets are 64-bit throughout (a 4K sequence of 130,686 tokens times 32
+ *     heads times 128 dims exceeds 2^31 bytes).
+ */
+#ifndef SOLATTN_H
+#define SOLATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define SOL_OK 0
+#define SOL_ERR_INVALID_ARG (-1) /* null pointer, size <= 0, NaN beta, short workspace, misalignment */
+#define SOL_ERR_UNSUPPORTED (-2) /* d != 128, B not in {64, 128}, unknown mode */
+#define SOL_ERR_HIP (-3)         /* the HIP runtime reported a launch error */
+
+/* modes of sol_attn_forward */
+#define SOL_DENSE 0  /* plain softmax attention; beta and B are ignored */
+#define SOL_SPARSE 1 /* thresholded block-sparse attention with the Taylor term */
+
+/*
+ * Block mean-pool of keys and values.
+ *   Sol-Engine LTX25 page, "Stage 2 Optimization -- Core Technology: Sol-Attn",
+ *   bullets "On-the-fly routing" (pooled keys) and "Proxy-score reuse".
+ * k, v     [H, N, d] bf16 (read).
+ * kbar     [H, nb, d] fp32 (written), nb = ceil(N / B): row j is the mean of
+ *          keys jB .. min(N, (j+1)B) - 1 (the last block may hold fewer than B
+ *          tokens; only real tokens are averaged).
+ * vbar     [H, nb, d] fp32 (written), the same for values.
+ * Pointers 16-byte aligned.
+ */
+int sol_attn_pool(const uint16_t* k, const uint16_t* v, float* kbar, float* vbar,
+                  int N, int H, int d, int B, void* stream);
+
+/*
+ * Row statistics of the block proxy scores (the first half of the routing).
+ *   Sol-Engine LTX25 page, "Stage 2 Optimization -- Core Technology: Sol-Attn",
+ *   bullet "Query-dependent thresholding".
+ * q        [H, N, d] bf16 query rows (read).
+ * kbar     [H, nb, d] fp32 pooled keys of Nk keys, nb = ceil(Nk / B) (read).
+ * mu       [H, N] fp32 (written): mean over j of p_ij = q_i . kbar_j / sqrt(d).
+ * sigma    [H, N] fp32 (written): population standard deviation of p_i. .
+ * The proxy map p is never stored.
+ */
+int sol_attn_row_stats(const uint16_t* q, const float* kbar, float* mu, float* sigma,
+                       int N, int Nk, int H, int d, int B, void* stream);
+
+/*
+ * Attention forward.
+ *   SOL_SPARSE: Sol-Engine LTX25 page, "Stage 2 Optimization -- Core
+ *   Technology: Sol-Attn" (all three bullets), with the Taylor weight above.
+ *   SOL_DENSE, or SOL_SPARSE with beta = -inf: plain softmax attention.
+ *   beta = +inf selects no block (every block enters through its Taylor term).
+ * q        [H, N, d] bf16, N query rows (read).
+ * k, v     [H, Nk, d] bf16, Nk key rows (read); Nk = 0 means Nk = N.
+ * out      [H, N, d] bf16 (written, round to nearest even).
+ * lse      [H, N] fp32 natural log of the full softmax denominator (exact plus
+ *          Taylor mass) relative to e^0, or NULL.
+ * B        key block size for SOL_SPARSE (64 or 128); ignored by SOL_DENSE.
+ * beta     threshold multiplier; NaN is an error.
+ * workspace, ws_bytes: device scratch of at least
+ *          sol_attn_workspace_size(N, Nk, H, d, B, mode) bytes, 256-byte
+ *          aligned (may be NULL when that size is 0).  Its contents on entry
+ *          are ignored; on return it holds kbar, vbar, mu, sigma (sparse) and
+ *          split partials.  Two calls in flight must not share a workspace.
+ * When few query tiles exist (short queries against long keys), the keys are
+ * split across workgroups and the partial answers are merged exactly
+ * (doubleAI page, "Attention across two GPUs").
+ */
+int sol_attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     uint16_t* out, float* lse, int N, int H, int d, int B,
+                     float beta, int mode, int Nk, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/* Bytes of workspace sol_attn_forward needs for these sizes (0 if none). */
+size_t sol_attn_workspace_size(int N, int Nk, int H, int d, int B, int mode);
+
+/*
+ * Exact merge of two partial answers over disjoint key sets.
+ *   doubleAI page, "Attention across two GPUs": each partial carries its
+ *   running maximum and sum of exponentials (here as lse) and merges exactly.
+ * out_a, out_b [H, N, d] bf16 and lse_a, lse_b [H, N] fp32 (read).
+ * out [H, N, d] bf16 and lse [H, N] fp32 (written):
+ *   lse = log(e^lse_a + e^lse_b), out = e^(lse_a-lse) out_a + e^(lse_b-lse) out_b.
+ * Both lse = -inf gives out = 0, lse = -inf.  out may alias out_a (or out_b)
+ * and lse may alias lse_a (or lse_b).
+ */
+int attn_lse_merge(const uint16_t* out_a, const float* lse_a, const uint16_t* out_b,
+                   const float* lse_b, uint16_t* out, float* lse, int N, int H, int d,
+                   void* stream);
+
+/* Static description of a return code (never NULL). */
+const char* sol_attn_error_string(int code);
+
+/*
+ * Inspection: proxy scores of a row range, p_ij = q_i . kbar_j / sqrt(d),
+ * computed by the same device code the forward kernel uses for routing.
+ *   Sol-Engine LTX25 page, "Stage 2 Optimization -- Core Technology: Sol-Attn".
+ * p        [H, nrows, nb] fp32 (written) for rows row0 .. row0 + nrows - 1.
+ */
+int sol_attn_proxy_scores(const uint16_t* q, const float* kbar, float* p, int row0,
+                          int nrows, int N, int Nk, int H, int d, int B, void* stream);
+
+/*
+ * Inspection: the block selection the forward kernel makes, for rows
+ * row0 .. row0 + nrows - 1 (row0 a multiple of 128), and density counts.
+ *   Sol-Engine LTX25 page, "Stage 2 Optimization -- Core Technology: Sol-Attn",
+ *   bullet "Query-dependent thresholding" (p_ij >= mu_i + beta sigma_i).
+ * mask     [H, nrows, nb] uint8 (written, 1 = attended exactly), or NULL.
+ * counts   int64[4] (written): selected (row, block) pairs; (32-row tile, block)
+ *          pairs with any selected row; (128-row tile, block) pairs with any
+ *          selected row; number of (128-row tile, block) pairs in the range.
+ * mu, sigma from sol_attn_row_stats.  beta as in sol_attn_forward.
+ */
+int sol_attn_block_mask(const uint16_t* q, const float* kbar, const float* mu,
+                        const float* sigma, float beta, int row0, int nrows, int N,
+                        int Nk, int H, int d, int B, uint8_t* mask, int64_t* counts,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOLATTN_H */

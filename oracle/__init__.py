@@ -136,13 +136,15 @@ def near_ties_ref(p: np.ndarray, mu: np.ndarray, sigma: np.ndarray, beta: float,
 def sol_attn_head_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int,
                       beta: float, rows: Optional[Sequence[int]] = None,
                       force: Optional[dict] = None, taylor: bool = True,
-                      chunk: int = 256):
+                      chunk: int = 256, pooled=None):
     """One head of Sol-Attn-style sparse attention, step by step [SOL].
 
     ``q`` ``[nq, d]``, ``k``/``v`` ``[nk, d]`` (float64).  ``rows`` restricts
     the computation to some query rows (rows are independent).  ``force`` keys
     are absolute row indices.  ``taylor=False`` drops the Taylor term (hard
-    selection), for quality comparisons only.
+    selection), for quality comparisons only.  ``pooled`` may pass the
+    ``(kbar, vbar)`` this function returned in ``info`` for the same keys, to
+    skip recomputing them.
 
     Returns ``(out [R, d], lse [R], info)`` where ``info`` holds ``p``, ``mu``,
     ``sigma`` and the selection ``mask`` of the computed rows.  A row whose
@@ -155,8 +157,11 @@ def sol_attn_head_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int,
     bounds = block_bounds(nk, B)
     n_j = np.array([e - s for s, e in bounds], dtype=np.float64)
     # step 1: pooled keys and values
-    kbar = pool_ref(k, B)
-    vbar = pool_ref(v, B)
+    if pooled is None:
+        kbar = pool_ref(k, B)
+        vbar = pool_ref(v, B)
+    else:
+        kbar, vbar = pooled
     # step 2: proxy scores for the requested rows
     qr = q[rows]
     p = proxy_ref(qr, kbar)
@@ -199,7 +204,7 @@ def sol_attn_head_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int,
         with np.errstate(invalid="ignore", divide="ignore"):
             out[r0:r1] = np.where(ok[:, None], num / den[:, None], np.nan)
             lse[r0:r1] = np.where(ok, M + np.log(np.where(ok, den, 1.0)), np.nan)
-    info = dict(p=p, mu=mu, sigma=sigma, mask=sel, rows=rows)
+    info = dict(p=p, mu=mu, sigma=sigma, mask=sel, rows=rows, pooled=(kbar, vbar))
     return out, lse, info
 
 

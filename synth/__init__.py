@@ -28,6 +28,7 @@ All tensors are rounded to bfloat16 with round-to-nearest-even and laid out
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Optional
 
@@ -49,10 +50,10 @@ __all__ = [
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (round to nearest, ties to even); return uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
-    out = r.astype(np.uint16)
+    u = x.view(np.uint32)
+    # finite inputs: u + 0x7FFF + lsb stays below 2^32
+    out = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+           >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         out[nan] = np.uint16(0x7FC0)
@@ -119,15 +120,25 @@ def clustered_head(n: int, d: int, block: int, centres: int, noise: float,
     return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
 
 
-def clustered(w: Workload, heads: Optional[list] = None):
-    """bf16 bits of (Q, K, V) ``[H, N, d]`` for a named workload (all heads by default)."""
+def clustered(w: Workload, heads: Optional[list] = None, threads: int = 8):
+    """bf16 bits of (Q, K, V) ``[H, N, d]`` for a named workload (all heads by default).
+
+    Heads are independent streams, so they are drawn on a thread pool."""
     hs = list(range(w.heads)) if heads is None else list(heads)
     n, d = w.n, w.head_dim
     Q = np.empty((len(hs), n, d), np.uint16)
     K = np.empty_like(Q)
     V = np.empty_like(Q)
-    for i, h in enumerate(hs):
-        Q[i], K[i], V[i] = clustered_head(n, d, w.block, w.centres, w.noise, w.seed, h)
+
+    def one(i):
+        Q[i], K[i], V[i] = clustered_head(n, d, w.block, w.centres, w.noise, w.seed, hs[i])
+
+    if threads > 1 and len(hs) > 1:
+        with ThreadPoolExecutor(min(threads, len(hs))) as ex:
+            list(ex.map(one, range(len(hs))))
+    else:
+        for i in range(len(hs)):
+            one(i)
     return Q, K, V
 
 
@@ -140,12 +151,16 @@ def cross_head(nq: int, nk: int, d: int, seed: int, h: int):
     return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
 
 
-def cross(heads: int, nq: int, nk: int, d: int, seed: int):
+def cross(heads: int, nq: int, nk: int, d: int, seed: int, threads: int = 8):
     Q = np.empty((heads, nq, d), np.uint16)
     K = np.empty((heads, nk, d), np.uint16)
     V = np.empty((heads, nk, d), np.uint16)
-    for h in range(heads):
+
+    def one(h):
         Q[h], K[h], V[h] = cross_head(nq, nk, d, seed, h)
+
+    with ThreadPoolExecutor(max(1, min(threads, heads))) as ex:
+        list(ex.map(one, range(heads)))
     return Q, K, V
 
 

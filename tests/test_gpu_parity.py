@@ -1,0 +1,255 @@
+"""GPU parity of every C-ABI entry point against the fp64 oracle, at sizes the
+oracle finishes in seconds that still span several tiles and a ragged tail.
+
+Tolerances (unit-scale V): out max abs <= 1e-2 and mean abs <= 1e-3; lse max
+abs <= 1e-3; selection masks exact except near-ties (|p - tau| < 1e-4 by the
+oracle's own scores); pooled means and proxy scores to fp32-level bounds
+stated per test.
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import block_sparse_attention_06_amd as sa  # noqa: E402
+import oracle as O  # noqa: E402
+from synth import clustered, clustered_head, gaussian, WORKLOADS  # noqa: E402
+from tests.parity_utils import (best_match, check_close, dev, host, mask_mismatch_ok,  # noqa: E402
+                                sparse_with_ties)
+
+pytestmark = pytest.mark.gpu
+
+INF = float("inf")
+
+
+def _head(bits, h):
+    return O.bf16_to_f64(bits[h])
+
+
+# ---------------------------------------------------------------------------
+# pooling and routing
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("H,N,B", [(2, 2048, 64), (3, 1000, 128), (1, 77, 64), (2, 128, 128)])
+def test_pool_parity(H, N, B):
+    Q, K, V = gaussian(H, N, 128, seed=40 + N)
+    kbar, vbar = sa.sol_attn_pool(dev(K), dev(V), B)
+    torch.cuda.synchronize()
+    for h in range(H):
+        kr = O.pool_ref(_head(K, h), B)
+        vr = O.pool_ref(_head(V, h), B)
+        # fp32 sum of <= 128 bf16 values, then one division
+        np.testing.assert_allclose(host(kbar[h]), kr, rtol=0, atol=2e-6)
+        np.testing.assert_allclose(host(vbar[h]), vr, rtol=0, atol=2e-6)
+
+
+@pytest.mark.parametrize("case", ["tiny_clustered", "gauss_ragged"])
+def test_proxy_and_stats_parity(case):
+    if case == "tiny_clustered":
+        w = WORKLOADS["tiny"]
+        Q, K, V = clustered(w)
+        B, N = w.block, w.n
+    else:
+        Q, K, V = gaussian(2, 1500, 128, seed=5)
+        B, N = 128, 1500
+    q, kk = dev(Q), dev(K)
+    kbar, _ = sa.sol_attn_pool(kk, dev(V), B)
+    p = sa.sol_attn_proxy_scores(q, kbar, B, N)
+    mu, sigma = sa.sol_attn_row_stats(q, kbar, B, N)
+    torch.cuda.synchronize()
+    for h in range(Q.shape[0]):
+        kb = O.pool_ref(_head(K, h), B)
+        pr = O.proxy_ref(_head(Q, h), kb)
+        mr, sr = O.row_stats_ref(pr)
+        # hi/lo split of kbar: ~16 significant bits -> |dp| well below the 1e-4 tie band
+        assert np.abs(host(p[h]) - pr).max() < 5e-5
+        assert np.abs(host(mu[h]) - mr).max() < 2e-5
+        assert np.abs(host(sigma[h]) - sr).max() < 2e-5
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5, 1.0, -0.5])
+def test_block_mask_parity(beta):
+    w = WORKLOADS["tiny"]
+    Q, K, V = clustered(w) if beta != -0.5 else gaussian(2, 2048, 128, seed=8)
+    B, N = w.block, w.n
+    q = dev(Q)
+    kbar, _ = sa.sol_attn_pool(dev(K), dev(V), B)
+    mu, sigma = sa.sol_attn_row_stats(q, kbar, B, N)
+    mask, counts = sa.sol_attn_block_mask(q, kbar, mu, sigma, beta, B, N)
+    torch.cuda.synchronize()
+    m = mask.cpu().numpy()
+    total_sel = 0
+    for h in range(Q.shape[0]):
+        kb = O.pool_ref(_head(K, h), B)
+        p = O.proxy_ref(_head(Q, h), kb)
+        mr, sr = O.row_stats_ref(p)
+        info = dict(p=p, mu=mr, sigma=sr, mask=O.select_ref(p, mr, sr, beta))
+        ok, n = mask_mismatch_ok(m[h], info, beta)
+        assert ok, f"head {h}: {n} mask mismatches outside the near-tie band"
+        total_sel += int(m[h].sum())
+    c = counts.cpu().numpy()
+    assert c[0] == total_sel
+    nb = (N + B - 1) // B
+    assert c[3] == Q.shape[0] * ((N + 127) // 128) * nb
+    assert c[0] <= 32 * c[1] and c[1] <= 4 * c[2] and c[2] <= c[3]
+
+
+# ---------------------------------------------------------------------------
+# forward: dense
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("H,N,Nk", [(2, 2048, 2048), (2, 300, 300), (1, 1, 1), (3, 126, 5000),
+                                    (2, 700, 129), (1, 130, 4097)])
+def test_dense_forward_parity(H, N, Nk):
+    Q, K, V = gaussian(H, N, 128, seed=N + Nk, nk=Nk)
+    out, lse = sa.sol_attn_forward(dev(Q), dev(K), dev(V), mode=sa.SOL_DENSE)
+    torch.cuda.synchronize()
+    for h in range(H):
+        o, l = O.dense_head_ref(_head(Q, h), _head(K, h), _head(V, h))
+        check_close(host(out[h]), o, host(lse[h]), l, what=f"dense H{H} N{N} Nk{Nk} h{h}")
+
+
+def test_dense_tiny_clustered():
+    w = WORKLOADS["tiny"]
+    Q, K, V = clustered(w)
+    out, lse = sa.sol_attn_forward(dev(Q), dev(K), dev(V), mode=sa.SOL_DENSE)
+    torch.cuda.synchronize()
+    o, l = O.dense_ref(Q, K, V)
+    check_close(host(out), o, host(lse), l, what="dense tiny")
+
+
+# ---------------------------------------------------------------------------
+# forward: sparse
+# ---------------------------------------------------------------------------
+
+
+def _sparse_case(Q, K, V, B, beta, heads=None, rows=None):
+    out, lse = sa.sol_attn_forward(dev(Q), dev(K), dev(V), B=B, beta=beta, mode=sa.SOL_SPARSE)
+    torch.cuda.synchronize()
+    go, gl = host(out), host(lse)
+    heads = range(Q.shape[0]) if heads is None else heads
+    for h in heads:
+        r = np.arange(Q.shape[1]) if rows is None else rows
+        o, l, info, cands = sparse_with_ties(_head(Q, h), _head(K, h), _head(V, h), B, beta, r)
+        ro, rl = best_match(go[h][r], gl[h][r], o, l, cands)
+        check_close(go[h][r], ro, gl[h][r], rl, what=f"sparse B{B} beta{beta} h{h}")
+    return go, gl
+
+
+@pytest.mark.parametrize("beta", [0.0, float("-inf")])
+def test_sparse_tiny_clustered(beta):
+    w = WORKLOADS["tiny"]
+    Q, K, V = clustered(w)
+    _sparse_case(Q, K, V, w.block, beta)
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5, 1.0, INF, -0.3])
+@pytest.mark.parametrize("B", [64, 128])
+def test_sparse_unclustered_taylor_heavy(beta, B):
+    """Unclustered N(0,1): the Taylor term carries a large share of the mass."""
+    Q, K, V = gaussian(2, 1000, 128, seed=77 + B)
+    _sparse_case(Q, K, V, B, beta)
+
+
+def test_sparse_ragged_and_short_query():
+    Q, K, V = gaussian(2, 250, 128, seed=3, nk=1234)
+    _sparse_case(Q, K, V, 128, 0.5)
+    Q, K, V = gaussian(1, 1, 128, seed=4, nk=200)
+    _sparse_case(Q, K, V, 64, 0.0)
+
+
+def test_sparse_split_keys_short_query():
+    """Few query tiles: the sparse key range is split over workgroups (chunks of
+    32 blocks) and merged; must match the unsplit oracle."""
+    Q, K, V = gaussian(2, 100, 128, seed=9, nk=64 * 200)
+    _sparse_case(Q, K, V, 64, 0.5)
+
+
+def test_sparse_neg_inf_is_dense_bitwise():
+    w = WORKLOADS["tiny"]
+    Q, K, V = clustered(w)
+    q, k, v = dev(Q), dev(K), dev(V)
+    o1, l1 = sa.sol_attn_forward(q, k, v, B=64, beta=float("-inf"), mode=sa.SOL_SPARSE)
+    o2, l2 = sa.sol_attn_forward(q, k, v, mode=sa.SOL_DENSE)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_all_blocks_selected_matches_dense_oracle():
+    Q, K, V = gaussian(2, 700, 128, seed=12)
+    out, lse = sa.sol_attn_forward(dev(Q), dev(K), dev(V), B=128, beta=-1e6, mode=sa.SOL_SPARSE)
+    torch.cuda.synchronize()
+    for h in range(2):
+        o, l = O.dense_head_ref(_head(Q, h), _head(K, h), _head(V, h))
+        check_close(host(out[h]), o, host(lse[h]), l, what="all-selected")
+
+
+def test_forward_deterministic():
+    w = WORKLOADS["tiny"]
+    Q, K, V = clustered(w)
+    q, k, v = dev(Q), dev(K), dev(V)
+    a = sa.sol_attn_forward(q, k, v, B=64, beta=0.0)
+    b = sa.sol_attn_forward(q, k, v, B=64, beta=0.0)
+    c = sa.sol_attn_forward(q, k, v, mode=sa.SOL_DENSE)
+    d = sa.sol_attn_forward(q, k, v, mode=sa.SOL_DENSE)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.equal(c[0], d[0]) and torch.equal(c[1], d[1])
+
+
+# ---------------------------------------------------------------------------
+# LSE merge
+# ---------------------------------------------------------------------------
+
+
+def test_lse_merge_parity_and_edges():
+    Q, K, V = gaussian(2, 126, 128, seed=21, nk=3000)
+    q, k, v = dev(Q), dev(K), dev(V)
+    oa, la = sa.sol_attn_forward(q, k[:, :1700].contiguous(), v[:, :1700].contiguous(),
+                                 mode=sa.SOL_DENSE)
+    ob, lb = sa.sol_attn_forward(q, k[:, 1700:].contiguous(), v[:, 1700:].contiguous(),
+                                 mode=sa.SOL_DENSE)
+    om, lm = sa.attn_lse_merge(oa, la, ob, lb)
+    torch.cuda.synchronize()
+    for h in range(2):
+        o, l = O.dense_head_ref(_head(Q, h), _head(K, h), _head(V, h))
+        check_close(host(om[h]), o, host(lm[h]), l, what="merge vs unsplit")
+        # the merge kernel itself against the oracle merge of the same bf16 inputs
+        ro, rl = O.lse_merge_ref(host(oa[h]), host(la[h]), host(ob[h]), host(lb[h]))
+        np.testing.assert_allclose(host(om[h]), ro, rtol=0, atol=4e-3 * np.abs(ro).max() + 1e-6)
+        np.testing.assert_allclose(host(lm[h]), rl, rtol=0, atol=1e-5)
+    # edges: both empty -> 0 / -inf; one empty -> the other
+    la2 = la.clone()
+    la2[0, :3] = -INF
+    lb2 = lb.clone()
+    lb2[0, :3] = -INF
+    lb2[1, :5] = -INF
+    om2, lm2 = sa.attn_lse_merge(oa, la2, ob, lb2)
+    torch.cuda.synchronize()
+    assert torch.all(om2[0, :3] == 0) and torch.all(torch.isneginf(lm2[0, :3]))
+    assert torch.equal(om2[1, :5], oa[1, :5]) and torch.equal(lm2[1, :5], la2[1, :5])
+    # in place on out_a / lse_a
+    oa_c, la_c = oa.clone(), la.clone()
+    sa.attn_lse_merge(oa_c, la_c, ob, lb, out=oa_c, lse=la_c)
+    torch.cuda.synchronize()
+    assert torch.equal(oa_c, om) and torch.equal(la_c, lm)
+
+
+# ---------------------------------------------------------------------------
+# argument errors reported, nothing launched
+# ---------------------------------------------------------------------------
+
+
+def test_error_codes_through_binding():
+    q = torch.zeros((1, 64, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sa.SolAttnError) as e:
+        sa.sol_attn_forward(q, q, q, B=32, beta=0.0)
+    assert e.value.code == -2
+    small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sa.SolAttnError) as e:
+        sa.sol_attn_forward(q, q, q, B=64, beta=0.0, workspace=small_ws)
+    assert e.value.code == -1
