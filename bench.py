@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * 4K Stage-2 self-attention, query-thresholded block-sparse with the Taylor
+    term (pool + row statistics + fused forward, one sol_attn_forward call):
+    H=32, N=130,686 (130,560 video + 126 audio tokens), d=128, B=128, beta=0.5;
+  * audio->video cross-attention, dense: 126 queries against the two halves of
+    130,560 video keys (65,280 each, split-KV inside each call) and the exact
+    LSE merge of the two partial answers.
+Inputs are resident in HBM before timing starts.  The metric is ms/call and
+dense-equivalent TFLOP/s (4 H N^2 d for self-attention, 4 H Nq Nk d for
+cross-attention) against the bf16 MFMA peak.
+
+Prints one JSON line.  Only one GPU is used; --gpus above 1 exits.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0
+METRIC = "ms/call + dense-equivalent TFLOP/s (% bf16 MFMA peak), 4K Stage-2 sparse attention"
+KERNEL_SOURCES = ["block_sparse_attention_06_amd/csrc/forward.hip",
+                  "block_sparse_attention_06_amd/csrc/device.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_sparse_4k_beta0.5_traffic.json")
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--beta", type=float, default=0.5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true", help="skip beta=1.0 and dense 4K lines")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(Q, K, V, B, beta, budget_s):
+    """The fp64 oracle (as is) on a bounded sample: whole 128-row query tiles,
+    spread over heads and positions, until about ``budget_s`` seconds of CPU
+    work.  Reported in the same unit, dense-equivalent TFLOP/s."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    H, N, d = Q.shape
+    nqt = (N + 127) // 128
+    rng = np.random.default_rng(0)
+    done_rows = 0
+    tiles = []
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and len(tiles) < 64:
+        h = int(rng.integers(H))
+        t = int(rng.integers(nqt))
+        rows = np.arange(t * 128, min(N, (t + 1) * 128))
+        q, k, v = (O.bf16_to_f64(x[h]) for x in (Q, K, V))
+        O.sol_attn_head_ref(q, k, v, B, beta, rows=rows)
+        done_rows += len(rows)
+        tiles.append((h, t))
+    el = time.perf_counter() - t0
+    flops = 4.0 * done_rows * N * d
+    full_s = el * (H * N) / done_rows
+    return {
+        "value": flops / el / 1e12,
+        "unit": "TFLOP/s (dense-equivalent)",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{len(tiles)} random 128-row query tiles (head, tile) of the 4K workload, "
+                  f"beta={beta}, fp64 numpy, {el:.1f} s wall",
+        "ms_per_call_extrapolated": full_s * 1e3,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs "
+              "are out of scope for this library", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_sparse_attention_06_amd as sa
+    from synth import CROSS, WORKLOADS, clustered, cross
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    w = WORKLOADS["4k"]
+    H, N, d, B = w.heads, w.n, w.head_dim, w.block
+    log(f"generating 4K inputs H={H} N={N}")
+    Q, K, V = clustered(w, threads=16)
+    q, k, v = to_dev(Q), to_dev(K), to_dev(V)
+    c = CROSS
+    log("generating cross-attention inputs")
+    Qc, Kc, Vc = cross(c["heads"], c["nq"], c["nk"], c["head_dim"], c["seed"], threads=16)
+    qc = to_dev(Qc)
+    s = c["split"]
+    kca, kcb = to_dev(Kc[:, :s]), to_dev(Kc[:, s:])
+    vca, vcb = to_dev(Vc[:, :s]), to_dev(Vc[:, s:])
+    del Kc, Vc
+
+    # every buffer allocated before timing
+    out = torch.empty_like(q)
+    lse = torch.empty((H, N), dtype=torch.float32, device=dev)
+    ws_self = torch.empty(sa.sol_attn_workspace_size(N, N, H, d, B, sa.SOL_SPARSE),
+                          dtype=torch.uint8, device=dev)
+    nq = c["nq"]
+    ws_a = torch.empty(max(1, sa.sol_attn_workspace_size(nq, s, H, d, B, sa.SOL_DENSE)),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, sa.sol_attn_workspace_size(nq, c["nk"] - s, H, d, B, sa.SOL_DENSE)),
+                       dtype=torch.uint8, device=dev)
+    oa = torch.empty_like(qc)
+    ob = torch.empty_like(qc)
+    om = torch.empty_like(qc)
+    la = torch.empty((H, nq), dtype=torch.float32, device=dev)
+    lb = torch.empty_like(la)
+    lm = torch.empty_like(la)
+    stream = torch.cuda.current_stream()
+
+    def self_attn(beta=args.beta, mode=sa.SOL_SPARSE):
+        sa.sol_attn_forward(q, k, v, B=B, beta=beta, mode=mode, workspace=ws_self, out=out,
+                            lse=lse)
+
+    def cross_attn():
+        sa.sol_attn_forward(qc, kca, vca, mode=sa.SOL_DENSE, workspace=ws_a, out=oa, lse=la)
+        sa.sol_attn_forward(qc, kcb, vcb, mode=sa.SOL_DENSE, workspace=ws_b, out=ob, lse=lb)
+        sa.attn_lse_merge(oa, la, ob, lb, out=om, lse=lm)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        self_attn()
+        cross_attn()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, HIP events on the launch stream around each part
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        self_attn()
+        ev[i][1].record(stream)
+        cross_attn()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    self_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
+    cross_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
+    step_ms = wall * 1e3 / args.steps
+    log(f"step {step_ms:.3f} ms  self {np.median(self_ms):.3f} ms  cross {np.median(cross_ms):.3f} ms")
+
+    # routing kernels alone (same kernels as inside the call), to split the call
+    nrep = max(3, args.steps)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3 * nrep)]
+    for i in range(nrep):
+        e[3 * i].record(stream)
+        kb_, vb_ = sa.sol_attn_pool(k, v, B)
+        e[3 * i + 1].record(stream)
+        mu, sigma = sa.sol_attn_row_stats(q, kb_, B, N)
+        e[3 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    pool_ms = float(np.median([e[3 * i].elapsed_time(e[3 * i + 1]) for i in range(nrep)]))
+    stats_ms = float(np.median([e[3 * i + 1].elapsed_time(e[3 * i + 2]) for i in range(nrep)]))
+    call_ms = float(np.mean(self_ms))
+    fwd_ms = call_ms - pool_ms - stats_ms
+
+    # achieved density (outside the timed region)
+    _, counts = sa.sol_attn_block_mask(q, kb_, mu, sigma, args.beta, B, N, want_mask=False)
+    cnt = counts.cpu().numpy().astype(np.int64)
+    nb = (N + B - 1) // B
+    rho_row = cnt[0] / (H * N * nb)
+    rho_tile32 = cnt[1] / (H * ((N + 31) // 32) * nb)
+    rho_tile128 = cnt[2] / cnt[3]
+
+    dense_flops = 4.0 * H * N * N * d
+    cross_flops = 4.0 * H * nq * c["nk"] * d
+    step_flops = dense_flops + cross_flops
+    value = step_flops / (step_ms * 1e-3) / 1e12
+    call_tflops = dense_flops / (call_ms * 1e-3) / 1e12
+
+    # roofline of the dominant kernel (fused sparse forward): algorithmic flops
+    # = 4 d n_j per selected (row, block) pair
+    alg_flops = 4.0 * d * B * cnt[0]
+    achieved = alg_flops / (fwd_ms * 1e-3) / 1e12
+    executed = 4.0 * d * B * 32 * cnt[1] / (fwd_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tf = json.load(open(TRAFFIC_FILE))
+            if tf.get("kernel_hash") == kernel_hash() and abs(tf.get("beta", -1) - args.beta) < 1e-9:
+                traffic = tf.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic}
+
+    extras = {}
+    if not args.no_extras:
+        for beta2 in (1.0,):
+            es = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            self_attn(beta2)
+            es[0].record(stream)
+            for _ in range(3):
+                self_attn(beta2)
+            es[1].record(stream)
+            torch.cuda.synchronize()
+            ms = es[0].elapsed_time(es[1]) / 3
+            _, c2 = sa.sol_attn_block_mask(q, kb_, mu, sigma, beta2, B, N, want_mask=False)
+            c2 = c2.cpu().numpy()
+            extras[f"4k_sparse_beta{beta2}"] = {
+                "ms_per_call": ms, "dense_equiv_tflops": dense_flops / ms / 1e9,
+                "rho_row": c2[0] / (H * N * nb), "rho_tile128": c2[2] / c2[3]}
+        es = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        es[0].record(stream)
+        for _ in range(2):
+            self_attn(float("-inf"), sa.SOL_DENSE)
+        es[1].record(stream)
+        torch.cuda.synchronize()
+        ms = es[0].elapsed_time(es[1]) / 2
+        extras["4k_dense"] = {"ms_per_call": ms, "tflops": dense_flops / ms / 1e9,
+                              "pct_bf16_peak": 100 * dense_flops / ms / 1e9 / PEAK_BF16_TFLOPS}
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu oracle baseline")
+        cpu = cpu_baseline(Q, K, V, B, args.beta, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s (dense-equivalent)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "4k-stage2-sparse-self-attention+audio-video-cross-attention",
+            "self": {"heads": H, "tokens": N, "head_dim": d, "block": B, "beta": args.beta,
+                     "centres": w.centres, "seed": w.seed},
+            "cross": {"heads": H, "queries": nq, "keys": c["nk"], "halves": [s, c["nk"] - s],
+                      "seed": c["seed"]},
+            "parallelism": "single-gpu",
+        },
+        "ms_per_call_4k_sparse": call_ms,
+        "dense_equiv_tflops_4k_sparse": call_tflops,
+        "pct_bf16_peak_4k_sparse": 100 * call_tflops / PEAK_BF16_TFLOPS,
+        "components_ms": {"pool": pool_ms, "row_stats": stats_ms, "fused_forward": fwd_ms,
+                          "cross_attention_halves_plus_merge": float(np.mean(cross_ms))},
+        "density": {"rho_row": rho_row, "rho_tile32": rho_tile32, "rho_tile128": rho_tile128},
+        "executed_tile_tflops": executed,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extras": extras,
+        "kernel_hash": kernel_hash(),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

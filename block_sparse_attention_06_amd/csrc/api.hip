@@ -47,7 +47,7 @@ Split plan_split(int N, int Nk, int H, int KB, bool sparse) {
 struct Plan {
   Split sp, dn;  // sparse plan (blocks of B) and dense plan (tiles of 128 keys)
   int max_splits;
-  size_t off_kbar, off_vbar, off_vsum, off_mu, off_sigma, off_po, off_pml, bytes;
+  size_t off_kbar, off_vbar, off_vsum, off_khi, off_klo, off_mu, off_sigma, off_po, off_pml, bytes;
 };
 
 // Sizes are validated by the caller.  A sparse-mode workspace also covers the
@@ -72,6 +72,8 @@ Plan make_plan(int N, int Nk, int H, int B, int mode) {
     p.off_kbar = take((size_t)H * p.sp.nb * 128 * sizeof(float));
     p.off_vbar = take((size_t)H * p.sp.nb * 128 * sizeof(float));
     p.off_vsum = take((size_t)H * 128 * p.sp.nb_pad * sizeof(uint16_t));
+    p.off_khi = take((size_t)H * p.sp.nb_pad * 128 * sizeof(uint16_t));
+    p.off_klo = take((size_t)H * p.sp.nb_pad * 128 * sizeof(uint16_t));
     p.off_mu = take(HN * sizeof(float));
     p.off_sigma = take(HN * sizeof(float));
   }
@@ -114,7 +116,7 @@ int sol_attn_pool(const uint16_t* k, const uint16_t* v, float* kbar, float* vbar
   if (int r = check_block(B)) return r;
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(kbar, 16) || !aligned(vbar, 16))
     return SOL_ERR_INVALID_ARG;
-  PoolArgs a{k, v, kbar, vbar, nullptr, N, H, B, cdiv(N, B), 0};
+  PoolArgs a{k, v, kbar, vbar, nullptr, nullptr, nullptr, N, H, B, cdiv(N, B), 0};
   return hip_status(launch_pool(a, (hipStream_t)stream));
 }
 
@@ -169,11 +171,12 @@ int sol_attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, ui
   f.total = H * f.n_qt * f.splits;
   if (sparse) {
     PoolArgs pa{k, v, (float*)(ws + p.off_kbar), (float*)(ws + p.off_vbar),
-                (uint16_t*)(ws + p.off_vsum), Nk, H, B, sp.nb, sp.nb_pad};
+                (uint16_t*)(ws + p.off_vsum), (uint16_t*)(ws + p.off_khi),
+                (uint16_t*)(ws + p.off_klo), Nk, H, B, sp.nb, sp.nb_pad};
     if (int r = hip_status(launch_pool(pa, s))) return r;
     StatsArgs sa{q, pa.kbar, (float*)(ws + p.off_mu), (float*)(ws + p.off_sigma), N, H, sp.nb};
     if (int r = hip_status(launch_stats(sa, s))) return r;
-    f.kbar = pa.kbar; f.vsumT = pa.vsumT; f.mu = sa.mu; f.sigma = sa.sigma;
+    f.khi = pa.khi; f.klo = pa.klo; f.vsumT = pa.vsumT; f.mu = sa.mu; f.sigma = sa.sigma;
   }
   if (f.splits > 1) {
     f.part_o = (float*)(ws + p.off_po);

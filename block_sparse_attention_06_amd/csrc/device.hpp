@@ -35,6 +35,14 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// Loads through the global address space (vector memory counter only; a
+// generic pointer would become a flat load, which also holds up LDS waits).
+template <class T>
+__device__ __forceinline__ T gload(const void* p) {
+  typedef const T __attribute__((address_space(1))) global_t;
+  return *(global_t*)p;
+}
+
 __device__ __forceinline__ float bf16_to_f32(u16 b) { return __uint_as_float((uint32_t)b << 16); }
 
 // Round to nearest even (finite inputs).
@@ -64,41 +72,37 @@ __device__ __forceinline__ void load_qfrag(QFrag& qf, const u16* qhead, int row,
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (valid) x = p[ks * 2 + g];
+    if (valid) x = gload<u32x4>(p + ks * 2 + g);
     qf.k[ks] = as_bf16x8(x);
   }
+}
+
+// Split of an fp32 value into bf16 hi + lo (both round to nearest even):
+// hi + lo carries ~16 significant bits.  Every producer of the bf16 parts of
+// the pooled keys uses this one function, so the parts are bit-identical
+// wherever they are formed.
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)x;
+  lo = (__bf16)(x - (float)hi);
 }
 
 // Proxy scores p = (q . kbar_j) / sqrt(d) of the wave's 32 rows against the 32
 // pooled keys b0 .. b0+31 (Sol-Engine LTX25 page, "Stage 2 Optimization --
 // Core Technology: Sol-Attn": block proxy scores from pooled keys).
-// kbar is fp32; it enters the bf16 MFMA as hi + lo bf16 parts (q is exact in
-// bf16), so p carries ~16 significant bits of kbar instead of 8.
+// kbar enters the bf16 MFMA as hi + lo bf16 parts (q is exact in bf16), so p
+// carries ~16 significant bits of kbar instead of 8.  `load(ks, hi, lo)`
+// supplies the A operand of k-step ks for block row b0 + (lane % 32).
 // Result element i of lane l: block b0 + acc_row(i, l/32), query row l % 32.
-// Blocks >= nb read a clamped row; callers ignore those elements.
-// Every kernel that routes uses this one function, so the proxy scores the
-// inspection exports report are the ones the forward kernel compares.
-__device__ __forceinline__ f32x16 proxy_chunk(const QFrag& qf, const float* kbar_head, int b0,
-                                              int nb, int lane) {
-  const int g = lane >> 5;
-  int blk = b0 + (lane & 31);
-  blk = blk < nb ? blk : nb - 1;
-  const f32x4* row = reinterpret_cast<const f32x4*>(kbar_head + (int64_t)blk * kHeadDim);
+// Every kernel that routes runs this same MFMA sequence on bit-identical
+// operands, so the proxy scores the inspection exports report are the ones
+// the forward kernel compares.
+template <class Load>
+__device__ __forceinline__ f32x16 proxy_tile(const QFrag& qf, Load load) {
   f32x16 acc = {};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    f32x4 x0 = row[ks * 4 + g * 2];
-    f32x4 x1 = row[ks * 4 + g * 2 + 1];
     bf16x8 hi, lo;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      __bf16 h0 = (__bf16)x0[e];
-      __bf16 h1 = (__bf16)x1[e];
-      hi[e] = h0;
-      hi[e + 4] = h1;
-      lo[e] = (__bf16)(x0[e] - (float)h0);
-      lo[e + 4] = (__bf16)(x1[e] - (float)h1);
-    }
+    load(ks, hi, lo);
     acc = mfma32(hi, qf.k[ks], acc);
     acc = mfma32(lo, qf.k[ks], acc);
   }
@@ -106,6 +110,53 @@ __device__ __forceinline__ f32x16 proxy_chunk(const QFrag& qf, const float* kbar
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] *= scale;
   return acc;
+}
+
+// Proxy tile from fp32 pooled keys in global memory (rows >= nb are clamped;
+// callers ignore those elements).
+__device__ __forceinline__ f32x16 proxy_chunk(const QFrag& qf, const float* kbar_head, int b0,
+                                              int nb, int lane) {
+  const int g = lane >> 5;
+  int blk = b0 + (lane & 31);
+  blk = blk < nb ? blk : nb - 1;
+  const f32x4* row = reinterpret_cast<const f32x4*>(kbar_head + (int64_t)blk * kHeadDim);
+  return proxy_tile(qf, [&](int ks, bf16x8& hi, bf16x8& lo) __attribute__((always_inline)) {
+    const f32x4 x0 = gload<f32x4>(row + ks * 4 + g * 2);
+    const f32x4 x1 = gload<f32x4>(row + ks * 4 + g * 2 + 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      __bf16 h, l;
+      split_bf16(x0[e], h, l);
+      hi[e] = h;
+      lo[e] = l;
+      split_bf16(x1[e], h, l);
+      hi[e + 4] = h;
+      lo[e + 4] = l;
+    }
+  });
+}
+
+// Proxy tile from the bf16 hi / lo parts of the pooled keys ([nb_pad, 128]
+// each, zero rows past nb), as the pool kernel writes them for the forward pass.
+__device__ __forceinline__ f32x16 proxy_chunk_hl(const QFrag& qf, const u16* khi_head,
+                                                 const u16* klo_head, int b0, int lane) {
+  const int g = lane >> 5;
+  const int64_t off = (int64_t)(b0 + (lane & 31)) * kHeadDim + g * 8;
+  return proxy_tile(qf, [&](int ks, bf16x8& hi, bf16x8& lo) __attribute__((always_inline)) {
+    hi = as_bf16x8(gload<u32x4>(khi_head + off + ks * 16));
+    lo = as_bf16x8(gload<u32x4>(klo_head + off + ks * 16));
+  });
+}
+
+// gfx950 transposing LDS read: in each group of 16 lanes, lane j reads 4
+// consecutive b16 values at its address; lane i of the group receives value
+// (i % 4) of lanes 4e + i/4 for e = 0..3.  With lane j pointing at
+// row r0 + j/4, column c0 + 4 (j % 4) of a row-major b16 matrix, lane i gets
+// the column c0 + i of rows r0 .. r0+3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const u16* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+  return __builtin_bit_cast(u32x2, r);
 }
 
 // Row threshold tau = mu + beta sigma (Sol-Engine LTX25 page, bullet

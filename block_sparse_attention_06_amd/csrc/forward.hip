@@ -5,33 +5,47 @@
 // Sol-Engine LTX25 page, "Stage 2 Optimization -- Core Technology: Sol-Attn":
 //  - routing is folded into the softmax pass: pooled keys are taken 32 blocks
 //    at a time ("chunk-wise"), their proxy scores are compared with each row's
-//    threshold, and only then are the chunk's key/value tiles fetched -- the
-//    proxy scores of a chunk live in registers and are never stored;
+//    threshold, and only the selected blocks' key/value tiles are fetched --
+//    the proxy scores of a chunk live in registers and are never stored;
 //  - rejected blocks contribute n_j e^{mu_i} (1 + p_ij - mu_i) on the pooled
 //    value (numerator) and the same weight (denominator).
 // doubleAI page, "Attention across two GPUs": with few query tiles the key
 // range is split over workgroups and the partial answers, each carrying its
 // running maximum and denominator, are merged exactly (combine_kernel).
 //
-// Workgroup: 4 waves x 32 query rows = 128 rows of one head.  Per key tile the
-// workgroup stages K (row-major) and V^T (transposed, keys permuted so an MFMA
-// operand is one 16-byte LDS read) in LDS; each wave then computes
-// S^T = K Q^T and O^T += V^T P^T on bf16 MFMA with fp32 accumulation.  A tile
-// is fetched when any wave of the workgroup selected the block, and a wave
-// issues its MFMAs only when one of its own 32 rows selected it; rows that did
-// not select it are masked to -inf inside the tile.
+// Workgroup: 4 waves x 32 query rows = 128 rows of one head; two workgroups
+// per CU.  Keys are processed in units of 64.  Each unit's K and V rows are
+// staged in LDS row-major (XOR-swizzled 16-byte chunks), double-buffered: the
+// next unit's global loads are issued into registers before the current unit
+// is computed and written to the other LDS buffer after it, with one barrier
+// per unit.  Each wave computes S^T = K Q^T and O^T += V^T P^T on bf16 MFMA
+// (fp32 accumulation); the V^T operand comes straight from the row-major tile
+// through the transposing LDS read.  A unit is fetched when any wave of the
+// workgroup selected its block; a wave issues MFMAs only when one of its own
+// 32 rows did, and rows that did not select it get zero probability.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace solattn {
 
+namespace {
+
+constexpr int kUnit = 64;             // keys per staged unit
+constexpr float kRescaleSlack = 8.f;  // log2 units the running reference may lag the max
+
+// LDS layouts of one 64-key unit ([64 rows][128 bf16], 16-byte chunks):
+// K rows put chunk c at c ^ (row % 16): the S operand reads 16 consecutive rows
+// at one chunk per LDS cycle.  V rows put chunk c at c ^ 4 (row % 4): the
+// transposing read takes 4 consecutive rows x 4 chunks per 16 lanes.
+__device__ __forceinline__ int k_off(int row, int c) { return row * kHeadDim + ((c ^ (row & 15)) << 3); }
+__device__ __forceinline__ int v_off(int row, int c) { return row * kHeadDim + ((c ^ ((row & 3) << 2)) << 3); }
+
+}  // namespace
+
 template <bool SPARSE, int KB>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
-  constexpr int KS = kHeadDim + 8;  // K tile row stride (bf16 elements)
-  constexpr int VS = KB + 8;        // V^T tile row stride
-  constexpr int NT = KB / 32;       // 32-key sub-tiles
-  __shared__ __attribute__((aligned(16))) u16 Ks[KB * KS];
-  __shared__ __attribute__((aligned(16))) u16 Vt[kHeadDim * VS];
+  __shared__ __attribute__((aligned(16))) u16 lds_k[2][kUnit * kHeadDim];
+  __shared__ __attribute__((aligned(16))) u16 lds_v[2][kUnit * kHeadDim];
   __shared__ uint32_t wmask[2][4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, r32 = lane & 31;
@@ -52,6 +66,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   load_qfrag(qf, a.q + (int64_t)h * a.N * kHeadDim, row, qvalid, g);
   const u16* kh = a.k + (int64_t)h * a.Nk * kHeadDim;
   const u16* vh = a.v + (int64_t)h * a.Nk * kHeadDim;
+  const int Nk = a.Nk;
 
   const int t_begin = split * a.tiles_per_split;
   const int t_end = min(a.nb, t_begin + a.tiles_per_split);
@@ -60,125 +75,132 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-  float l = 0.f;   // this lane's share of the denominator, relative to 2^m
-  float m;         // running maximum (log2 units)
+  float l = 0.f;  // this lane's share of the denominator, relative to 2^m
+  float m;        // reference of the running sums (log2 units), within kRescaleSlack of the max
   float mu = 0.f, tau = __builtin_inff();
   if constexpr (SPARSE) {
     if (qvalid) {
-      mu = a.mu[(int64_t)h * a.N + row];
-      tau = make_tau(mu, a.sigma[(int64_t)h * a.N + row], a.beta);
+      mu = gload<float>(a.mu + (int64_t)h * a.N + row);
+      tau = make_tau(mu, gload<float>(a.sigma + (int64_t)h * a.N + row), a.beta);
     }
-    m = mu * kLog2e;  // the Taylor terms are relative to e^mu: start the reference there
+    m = mu * kLog2e;  // Taylor terms are relative to e^mu: start the reference there
   } else {
     m = -__builtin_inff();
   }
 
-  // ---- stage one key tile (K row-major, V transposed) in LDS ----
-  auto load_tile = [&](int tile) {
-    const int key0 = tile * KB;
+  // ---- staging: 64 rows x 16 chunks of K and of V, 4 + 4 chunks per thread ----
+  u32x4 stg[8];
+  // Rows past the last key re-read the last key (finite data): their scores are
+  // masked and their probabilities are zero, so no load needs a predicate.
+  auto issue_loads = [&](int key0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int rep = 0; rep < KB / 16; ++rep) {
-      const int u = tid + 256 * rep, r = u >> 4, c = u & 15;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key0 + r < a.Nk)
-        x = *reinterpret_cast<const u32x4*>(kh + (int64_t)(key0 + r) * kHeadDim + c * 8);
-      *reinterpret_cast<u32x4*>(&Ks[r * KS + c * 8]) = x;
+    for (int rep = 0; rep < 4; ++rep) {
+      const int idx = tid + 256 * rep, r = idx >> 4, c = idx & 15;
+      const int64_t off = (int64_t)min(key0 + r, Nk - 1) * kHeadDim + c * 8;
+      stg[rep] = gload<u32x4>(kh + off);
+      stg[4 + rep] = gload<u32x4>(vh + off);
     }
+  };
+  auto write_lds = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int rep = 0; rep < KB / 64; ++rep) {
-      const int u = tid + 256 * rep, c = u & 15, quad = u >> 4;
-      u32x4 x[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = key0 + quad * 4 + r;
-        x[r] = u32x4{0u, 0u, 0u, 0u};
-        if (key < a.Nk) x[r] = *reinterpret_cast<const u32x4*>(vh + (int64_t)key * kHeadDim + c * 8);
-      }
-      const int qq = quad & 3;
-      const int col = (quad >> 2) * 16 + (qq & 1) * 8 + (qq >> 1) * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        u32x2 lo, hi;
-        lo[0] = (x[0][e] & 0xffffu) | (x[1][e] << 16);
-        lo[1] = (x[2][e] & 0xffffu) | (x[3][e] << 16);
-        hi[0] = (x[0][e] >> 16) | (x[1][e] & 0xffff0000u);
-        hi[1] = (x[2][e] >> 16) | (x[3][e] & 0xffff0000u);
-        *reinterpret_cast<u32x2*>(&Vt[(c * 8 + 2 * e) * VS + col]) = lo;
-        *reinterpret_cast<u32x2*>(&Vt[(c * 8 + 2 * e + 1) * VS + col]) = hi;
-      }
+    for (int rep = 0; rep < 4; ++rep) {
+      const int idx = tid + 256 * rep, r = idx >> 4, c = idx & 15;
+      *reinterpret_cast<u32x4*>(&lds_k[st][k_off(r, c)]) = stg[rep];
+      *reinterpret_cast<u32x4*>(&lds_v[st][v_off(r, c)]) = stg[4 + rep];
     }
   };
 
-  // ---- exact online-softmax update with one staged tile ----
-  auto compute_tile = [&](int tile, bool mine) {
-    f32x16 s[NT];
+  // ---- exact online-softmax update with one staged unit ----
+  auto compute = [&](int st, int key0, bool mine) __attribute__((always_inline)) {
+    f32x16 s[2];
 #pragma unroll
-    for (int kt = 0; kt < NT; ++kt) {
+    for (int kt = 0; kt < 2; ++kt) {
       s[kt] = f32x16{};
+      const int r = kt * 32 + r32;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        u32x4 ka = *reinterpret_cast<const u32x4*>(&Ks[(kt * 32 + r32) * KS + ks * 16 + g * 8]);
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(&lds_k[st][k_off(r, ks * 2 + g)]);
         s[kt] = mfma32(as_bf16x8(ka), qf.k[ks], s[kt]);
       }
     }
-    const int key0 = tile * KB;
+    if (key0 + kUnit > Nk) {  // ragged last unit: keys past the end do not exist
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (key0 + kt * 32 + acc_row(i, g) >= Nk) s[kt][i] = -__builtin_inff();
+    }
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int kt = 0; kt < NT; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = key0 + kt * 32 + acc_row(i, g);
-        const float x = (mine && key < a.Nk) ? s[kt][i] * sl2 : -__builtin_inff();
-        s[kt][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float mref = mn == -__builtin_inff() ? 0.f : mn;
-    const float alpha = fast_exp2(m - mref);
-    m = mn;
-    l *= alpha;
+    const float mc = mx * sl2;
+    // move the reference only when the max outruns it by more than the slack
+    const bool up = mine && (mc > m + kRescaleSlack);
+    if (__ballot(up)) {
+      const float alpha = up ? fast_exp2(m - mc) : 1.f;
+      l *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-    bf16x8 pb[NT * 2];
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+    }
+    if (up) m = mc;
+    const float neg_ref = mine ? -m : -__builtin_inff();  // rows that did not select: p = 0
+    bf16x8 pb[4];
     float rs = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < NT; ++kt) {
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pe = fast_exp2(s[kt][i] - mref);
+        const float pe = fast_exp2(__builtin_fmaf(s[kt][i], sl2, neg_ref));
         rs += pe;
         pb[kt * 2 + (i >> 3)][i & 7] = (__bf16)pe;
       }
     }
     l += rs;
+    // O^T += V^T P^T: the V^T operand of k-step (kt, h2) holds keys
+    // kt*32 + h2*16 + {4g..4g+3, 8+4g..8+4g+3} -- the keys of P that this lane
+    // half holds -- read as two transposed 4 x 16 blocks per 16-lane group.
+    const int G = lane >> 4, j = lane & 15;
 #pragma unroll
-    for (int kt = 0; kt < NT; ++kt) {
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
+        const int r0 = kt * 32 + h2 * 16 + g * 4 + (j >> 2);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          u32x4 va = *reinterpret_cast<const u32x4*>(
-              &Vt[(dt * 32 + r32) * VS + kt * 32 + h2 * 16 + g * 8]);
+          const int col = dt * 32 + (G & 1) * 16 + 4 * (j & 3);
+          const u32x2 v0 = lds_read_tr16(&lds_v[st][v_off(r0, col >> 3) + (col & 7)]);
+          const u32x2 v1 = lds_read_tr16(&lds_v[st][v_off(r0 + 8, col >> 3) + (col & 7)]);
+          const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
           o[dt] = mfma32(as_bf16x8(va), pb[kt * 2 + h2], o[dt]);
         }
       }
     }
   };
 
+  // ---- the stream of units: key offset, and whether this row / this wave take it ----
+  struct Unit {
+    int key0;
+    bool mine, need;
+  };
+
   if constexpr (SPARSE) {
-    const float* kb = a.kbar + (int64_t)h * a.nb * kHeadDim;
+    const u16* khi = a.khi + (int64_t)h * a.nb_pad * kHeadDim;
+    const u16* klo = a.klo + (int64_t)h * a.nb_pad * kHeadDim;
     const u16* vsum = a.vsumT + (int64_t)h * kHeadDim * a.nb_pad;
-    int parity = 0;
-    for (int c0 = t_begin; c0 < t_end; c0 += kChunk, parity ^= 1) {
-      // routing: proxy scores of this chunk, selection, Taylor weights
-      const f32x16 p = proxy_chunk(qf, kb, c0, a.nb, lane);
-      const float f = fast_exp2(mu * kLog2e - m);  // e^{mu - M}: Taylor terms at the current reference
+    // Route one chunk of 32 blocks: proxy scores, selection, Taylor part of
+    // the rejected blocks (at the current reference m).  Returns the blocks any
+    // row of the workgroup selected; `full` = this row's, `wv` = this wave's.
+    auto route = [&](int c0, int parity, uint32_t& full, uint32_t& wv)
+        __attribute__((always_inline)) -> uint32_t {
+      const f32x16 p = proxy_chunk_hl(qf, khi, klo, c0, lane);
+      const float f = fast_exp2(mu * kLog2e - m);  // e^{mu} relative to the reference
       uint32_t mine = 0;
-      // Weights of the rejected blocks enter the MFMA as bf16 hi + lo parts:
-      // when many blocks share nearly the same weight, a single bf16 rounding
-      // would bias the Taylor mass coherently instead of averaging out.
+      // Weights enter the MFMA as bf16 hi + lo parts: when many blocks share
+      // nearly the same weight, a single bf16 rounding would bias the Taylor
+      // mass coherently instead of averaging out.
       bf16x8 whi[2], wlo[2];
       float wden = 0.f;
 #pragma unroll
@@ -189,10 +211,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         const bool sel = inr && is_selected(p[i], tau);
         mine |= (uint32_t)sel << off;
         const float wt = (inr && !sel) ? (1.f + p[i] - mu) * f : 0.f;
-        const __bf16 wh = (__bf16)wt;
+        __bf16 wh, wl;
+        split_bf16(wt, wh, wl);
         whi[i >> 3][i & 7] = wh;
-        wlo[i >> 3][i & 7] = (__bf16)(wt - (float)wh);
-        const int nj = inr ? min(KB, a.Nk - blk * KB) : 0;
+        wlo[i >> 3][i & 7] = wl;
+        const int nj = inr ? min(KB, Nk - blk * KB) : 0;
         wden = __builtin_fmaf((float)nj, wt, wden);
       }
       // Taylor part: O^T += (block sums of V)^T W^T over the chunk, on MFMA
@@ -200,36 +223,96 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          u32x4 va = *reinterpret_cast<const u32x4*>(
-              vsum + (int64_t)(dt * 32 + r32) * a.nb_pad + c0 + h2 * 16 + g * 8);
+          const u32x4 va = gload<u32x4>(vsum + (int64_t)(dt * 32 + r32) * a.nb_pad + c0 + h2 * 16 + g * 8);
           o[dt] = mfma32(as_bf16x8(va), whi[h2], o[dt]);
           o[dt] = mfma32(as_bf16x8(va), wlo[h2], o[dt]);
         }
       }
       l += wden;
-      // blocks wanted by this row, by this wave, by the workgroup
-      const uint32_t full = mine | __shfl_xor(mine, 32);
-      uint32_t wu = full;
+      full = mine | __shfl_xor(mine, 32);
+      uint32_t w = full;
 #pragma unroll
-      for (int sh = 1; sh < 32; sh <<= 1) wu |= __shfl_xor(wu, sh);
-      if (lane == 0) wmask[parity][wave] = wu;
+      for (int sh = 1; sh < 32; sh <<= 1) w |= __shfl_xor(w, sh);
+      wv = w;
+      if (lane == 0) wmask[parity][wave] = w;
       __syncthreads();
-      uint32_t todo = wmask[parity][0] | wmask[parity][1] | wmask[parity][2] | wmask[parity][3];
-      while (todo) {
-        const int bo = __builtin_ctz(todo);
-        todo &= todo - 1;
-        __syncthreads();
-        load_tile(c0 + bo);
-        __syncthreads();
-        if ((wu >> bo) & 1u) compute_tile(c0 + bo, (full >> bo) & 1u);
+      return wmask[parity][0] | wmask[parity][1] | wmask[parity][2] | wmask[parity][3];
+    };
+
+    // chunk A is being consumed; chunk B (the next one) is already routed
+    int cA = t_begin, cB = t_begin + kChunk;
+    uint32_t fullA, wvA, fullB = 0, wvB = 0, UB = 0;
+    uint32_t UA = route(cA, 0, fullA, wvA);
+    if (cB < t_end) UB = route(cB, 1, fullB, wvB);
+    int pend = -1;  // second half of a 128-key block still to come
+    bool pend_mine = false, pend_need = false;
+    auto next = [&](Unit& u) __attribute__((always_inline)) -> bool {
+      if (KB == 128 && pend >= 0) {
+        u = Unit{pend, pend_mine, pend_need};
+        pend = -1;
+        return true;
       }
+      while (true) {
+        if (UA) {
+          const int b = __builtin_ctz(UA);
+          UA &= UA - 1;
+          u = Unit{(cA + b) * KB, ((fullA >> b) & 1u) != 0, ((wvA >> b) & 1u) != 0};
+          if (KB == 128) {
+            pend = u.key0 + kUnit;
+            pend_mine = u.mine;
+            pend_need = u.need;
+          }
+          return true;
+        }
+        if (cB >= t_end) return false;
+        cA = cB;
+        UA = UB;
+        fullA = fullB;
+        wvA = wvB;
+        cB += kChunk;
+        UB = 0;
+        if (cB < t_end) UB = route(cB, ((cB - t_begin) / kChunk) & 1, fullB, wvB);
+      }
+    };
+
+    Unit cur, nxt;
+    bool have = next(cur);
+    int st = 0;
+    if (have) {
+      issue_loads(cur.key0);
+      write_lds(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // as in the dense loop: nothing outstanding at loop entry
+    __syncthreads();
+    while (have) {
+      const bool hn = next(nxt);
+      if (hn) issue_loads(nxt.key0);
+      if (cur.need) compute(st, cur.key0, cur.mine);
+      if (hn) write_lds(st ^ 1);
+      __syncthreads();
+      st ^= 1;
+      cur = nxt;
+      have = hn;
     }
   } else {
-    for (int tile = t_begin; tile < t_end; ++tile) {
+    const int u_begin = t_begin * (KB / kUnit);
+    const int u_end = min(t_end * (KB / kUnit), (Nk + kUnit - 1) / kUnit);
+    int st = 0;
+    if (u_begin < u_end) {
+      issue_loads(u_begin * kUnit);
+      write_lds(0);
+    }
+    // Drain every load issued so far (query fragment included) on all paths, so
+    // the loop's only outstanding loads are the prefetches its LDS writes wait for.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int u = u_begin; u < u_end; ++u) {
+      const bool hn = u + 1 < u_end;
+      if (hn) issue_loads((u + 1) * kUnit);
+      compute(st, u * kUnit, true);
+      if (hn) write_lds(st ^ 1);
       __syncthreads();
-      load_tile(tile);
-      __syncthreads();
-      compute_tile(tile, true);
+      st ^= 1;
     }
   }
 

@@ -12,6 +12,8 @@ struct PoolArgs {
   float* kbar;      // [H, nb, 128]
   float* vbar;      // [H, nb, 128]
   uint16_t* vsumT;  // [H, 128, nb_pad] bf16 block sums, permuted groups of 16; may be null
+  uint16_t* khi;    // [H, nb_pad, 128] bf16 hi part of kbar (zero rows past nb); may be null
+  uint16_t* klo;    // [H, nb_pad, 128] bf16 lo part
   int N, H, B, nb, nb_pad;
 };
 
@@ -47,7 +49,8 @@ struct FwdArgs {
   const uint16_t* v;
   uint16_t* out;
   float* lse;          // may be null
-  const float* kbar;   // sparse only
+  const uint16_t* khi;  // sparse only: bf16 parts of the pooled keys
+  const uint16_t* klo;
   const uint16_t* vsumT;
   const float* mu;
   const float* sigma;

@@ -23,10 +23,16 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   __shared__ float part[16][kHeadDim + 4];
   const int j = blockIdx.x, h = blockIdx.y, which = blockIdx.z;
   const int tid = threadIdx.x, chunk = tid & 15, rg = tid >> 4;
-  if (j >= a.nb) {  // zero padding of the transposed block sums
-    if (which == 1 && a.vsumT && tid < kHeadDim) {
-      int pj = (j & ~15) + perm16(j & 15);
-      a.vsumT[((int64_t)h * kHeadDim + tid) * a.nb_pad + pj] = 0;
+  if (j >= a.nb) {  // zero padding of the forward pass's bf16 copies
+    if (tid < kHeadDim) {
+      if (which == 1 && a.vsumT) {
+        const int pj = (j & ~15) + perm16(j & 15);
+        a.vsumT[((int64_t)h * kHeadDim + tid) * a.nb_pad + pj] = 0;
+      }
+      if (which == 0 && a.khi) {
+        a.khi[((int64_t)h * a.nb_pad + j) * kHeadDim + tid] = 0;
+        a.klo[((int64_t)h * a.nb_pad + j) * kHeadDim + tid] = 0;
+      }
     }
     return;
   }
@@ -60,14 +66,20 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
     float* dst = which ? a.vbar : a.kbar;
     dst[((int64_t)h * a.nb + j) * kHeadDim + tid] = mean;
     if (which == 1 && a.vsumT) {
-      int pj = (j & ~15) + perm16(j & 15);
+      const int pj = (j & ~15) + perm16(j & 15);
       a.vsumT[((int64_t)h * kHeadDim + tid) * a.nb_pad + pj] = f32_to_bf16_bits(s);
+    }
+    if (which == 0 && a.khi) {
+      __bf16 hi, lo;
+      split_bf16(mean, hi, lo);
+      a.khi[((int64_t)h * a.nb_pad + j) * kHeadDim + tid] = __builtin_bit_cast(u16, hi);
+      a.klo[((int64_t)h * a.nb_pad + j) * kHeadDim + tid] = __builtin_bit_cast(u16, lo);
     }
   }
 }
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s) {
-  dim3 grid(a.vsumT ? a.nb_pad : a.nb, a.H, 2);
+  dim3 grid((a.vsumT || a.khi) ? a.nb_pad : a.nb, a.H, 2);
   if (a.B == 64)
     pool_kernel<64><<<grid, 256, 0, s>>>(a);
   else
@@ -77,12 +89,16 @@ hipError_t launch_pool(const PoolArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // Row statistics mu_i, sigma_i of p_i. over all key blocks.  One wave per 32
-// query rows, four waves per workgroup.  Proxy tiles come from proxy_chunk;
-// the sums are shifted by the row's first proxy p_i0 so the variance has no
+// query rows, four waves per workgroup.  Each chunk of 32 pooled keys is split
+// into bf16 hi / lo parts once per workgroup and staged in LDS (16-byte chunk
+// c of row r at c ^ (r % 16)), then every wave runs the proxy MFMA sequence on
+// it.  Sums are shifted by the row's first proxy p_i0 so the variance has no
 // cancellation, then reduced over the two lane halves.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5;
+  __shared__ __attribute__((aligned(16))) u16 khi[kChunk * kHeadDim];
+  __shared__ __attribute__((aligned(16))) u16 klo[kChunk * kHeadDim];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
   const int h = blockIdx.y;
   const int row = blockIdx.x * kQTile + wave * 32 + (lane & 31);
   const bool valid = row < a.N;
@@ -91,12 +107,41 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
   const float* kb = a.kbar + (int64_t)h * a.nb * kHeadDim;
   float shift = 0.f, s1 = 0.f, s2 = 0.f;
   for (int b0 = 0; b0 < a.nb; b0 += kChunk) {
-    f32x16 p = proxy_chunk(qf, kb, b0, a.nb, lane);
+    __syncthreads();
+    // 32 rows x 16 chunks of 8 values: two chunks per thread
+#pragma unroll
+    for (int rep = 0; rep < 2; ++rep) {
+      const int idx = tid + 256 * rep, r = idx >> 4, c = idx & 15;
+      const int blk = min(b0 + r, a.nb - 1);
+      const f32x4* src = reinterpret_cast<const f32x4*>(kb + (int64_t)blk * kHeadDim + c * 8);
+      const f32x4 x0 = src[0], x1 = src[1];
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        __bf16 hh, ll;
+        split_bf16(x0[e], hh, ll);
+        hi[e] = hh;
+        lo[e] = ll;
+        split_bf16(x1[e], hh, ll);
+        hi[e + 4] = hh;
+        lo[e + 4] = ll;
+      }
+      const int off = r * kHeadDim + ((c ^ (r & 15)) << 3);
+      *reinterpret_cast<bf16x8*>(&khi[off]) = hi;
+      *reinterpret_cast<bf16x8*>(&klo[off]) = lo;
+    }
+    __syncthreads();
+    const int r = lane & 31;
+    const f32x16 p = proxy_tile(qf, [&](int ks, bf16x8& hi, bf16x8& lo) __attribute__((always_inline)) {
+      const int off = r * kHeadDim + (((ks * 2 + g) ^ (r & 15)) << 3);
+      hi = *reinterpret_cast<const bf16x8*>(&khi[off]);
+      lo = *reinterpret_cast<const bf16x8*>(&klo[off]);
+    });
     if (b0 == 0) shift = __shfl(p[0], lane & 31);  // block 0 sits in element 0 of lane half 0
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (b0 + acc_row(i, g) < a.nb) {
-        float x = p[i] - shift;
+        const float x = p[i] - shift;
         s1 += x;
         s2 = __builtin_fmaf(x, x, s2);
       }
@@ -105,9 +150,9 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
   s1 += __shfl_xor(s1, 32);
   s2 += __shfl_xor(s2, 32);
   if (g == 0 && valid) {
-    float inv = 1.f / (float)a.nb;
-    float md = s1 * inv;
-    float var = __builtin_fmaf(-md, md, s2 * inv);
+    const float inv = 1.f / (float)a.nb;
+    const float md = s1 * inv;
+    const float var = __builtin_fmaf(-md, md, s2 * inv);
     a.mu[(int64_t)h * a.N + row] = shift + md;
     a.sigma[(int64_t)h * a.N + row] = sqrtf(fmaxf(var, 0.f));
   }
