@@ -31,6 +31,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 fl
 PEAK_HBM_GBS = 8000.0
 METRIC = "ms/call + dense-equivalent TFLOP/s (% bf16 MFMA peak), 4K Stage-2 sparse attention"
 KERNEL_SOURCES = ["block_sparse_attention_06_amd/csrc/forward.hip",
+                  "block_sparse_attention_06_amd/csrc/forward_pp.hip",
                   "block_sparse_attention_06_amd/csrc/device.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_sparse_4k_beta0.5_traffic.json")
 
@@ -53,6 +54,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true", help="skip beta=1.0 and dense 4K lines")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run three plain 1 GiB device-to-device copies (reference "
+                         "kernel of known traffic for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -111,6 +115,13 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def to_dev(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)

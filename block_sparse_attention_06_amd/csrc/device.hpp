@@ -101,6 +101,9 @@ __device__ __forceinline__ f32x16 proxy_tile(const QFrag& qf, Load load) {
   f32x16 acc = {};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
+    // operands in two batches of four k-steps: bounds the registers held by
+    // loads in flight inside the forward kernel
+    if (ks == 4) __builtin_amdgcn_sched_barrier(0);
     bf16x8 hi, lo;
     load(ks, hi, lo);
     acc = mfma32(hi, qf.k[ks], acc);
@@ -146,6 +149,25 @@ __device__ __forceinline__ f32x16 proxy_chunk_hl(const QFrag& qf, const u16* khi
     hi = as_bf16x8(gload<u32x4>(khi_head + off + ks * 16));
     lo = as_bf16x8(gload<u32x4>(klo_head + off + ks * 16));
   });
+}
+
+// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at LDS
+// byte address lds_base + 16 l (lds_base must be wave-uniform; it goes through
+// M0).  Issued through inline assembly on purpose: the compiler then does not
+// treat it as a pending write to every LDS location, and does not hold the
+// following LDS reads of other buffers until it lands.  The caller orders it
+// with explicit vector-memory waits (s_waitcnt vmcnt) and barriers.
+__device__ __forceinline__ void dma_to_lds16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+template <class T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(const char*)p;
 }
 
 // gfx950 transposing LDS read: in each group of 16 lanes, lane j reads 4

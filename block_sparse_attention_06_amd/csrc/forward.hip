@@ -14,15 +14,16 @@
 // running maximum and denominator, are merged exactly (combine_kernel).
 //
 // Workgroup: 4 waves x 32 query rows = 128 rows of one head; two workgroups
-// per CU.  Keys are processed in units of 64.  Each unit's K and V rows are
-// staged in LDS row-major (XOR-swizzled 16-byte chunks), double-buffered: the
-// next unit's global loads are issued into registers before the current unit
-// is computed and written to the other LDS buffer after it, with one barrier
-// per unit.  Each wave computes S^T = K Q^T and O^T += V^T P^T on bf16 MFMA
-// (fp32 accumulation); the V^T operand comes straight from the row-major tile
-// through the transposing LDS read.  A unit is fetched when any wave of the
-// workgroup selected its block; a wave issues MFMAs only when one of its own
-// 32 rows did, and rows that did not select it get zero probability.
+// per CU.  Keys stream through LDS in units of 32 rows of K and V, in a ring of
+// five stages filled by direct global->LDS loads four units ahead of the unit
+// being computed (no registers hold data in flight; each wave waits only for
+// its own loads of the next unit, then one barrier per unit publishes it).
+// Rows sit row-major with XOR-swizzled 16-byte chunks.  Each wave computes
+// S^T = K Q^T and O^T += V^T P^T on bf16 MFMA (fp32 accumulation); the V^T
+// operand comes straight from the row-major tile through the transposing LDS
+// read.  A unit is fetched when any wave of the workgroup selected its block;
+// a wave issues MFMAs only when one of its own 32 rows did, and rows that did
+// not select it get zero probability.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -30,31 +31,60 @@ namespace solattn {
 
 namespace {
 
-constexpr int kUnit = 64;             // keys per staged unit
-constexpr float kRescaleSlack = 8.f;  // log2 units the running reference may lag the max
+constexpr int kUnit = 32;                        // keys per staged unit
+constexpr int kStageElems = kUnit * kHeadDim;    // bf16 per tensor per stage
+constexpr float kRescaleSlack = 8.f;             // log2 units the reference may lag the max
 
-// LDS layouts of one 64-key unit ([64 rows][128 bf16], 16-byte chunks):
-// K rows put chunk c at c ^ (row % 16): the S operand reads 16 consecutive rows
-// at one chunk per LDS cycle.  V rows put chunk c at c ^ 4 (row % 4): the
-// transposing read takes 4 consecutive rows x 4 chunks per 16 lanes.
-__device__ __forceinline__ int k_off(int row, int c) { return row * kHeadDim + ((c ^ (row & 15)) << 3); }
-__device__ __forceinline__ int v_off(int row, int c) { return row * kHeadDim + ((c ^ ((row & 3) << 2)) << 3); }
+// LDS layouts of a unit ([32 rows][128 bf16], 16-byte chunks): K rows put
+// chunk c at c ^ (row % 16), so the S operand reads 16 consecutive rows at one
+// chunk without bank conflicts; V rows put chunk c at c ^ 4 (row % 4), so the
+// transposing read of 4 consecutive rows x 4 chunks per 16 lanes is
+// conflict-free.
+__device__ __forceinline__ int k_slot(int row, int c) { return c ^ (row & 15); }
+__device__ __forceinline__ int v_slot(int row, int c) { return c ^ ((row & 3) << 2); }
+
+// LDS ring depth: two workgroups per CU share 160 KiB.  Dense mode uses five
+// 16 KiB stages (loads four units ahead); sparse mode needs a few bytes for the
+// routing masks and uses four (three units ahead).
+template <bool SPARSE>
+constexpr int stages() { return SPARSE ? 4 : 5; }
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt(4 x (stages - 2)) -- this wave's
+// loads of the next unit done while the later units' stay in flight -- and
+// lgkmcnt(0) alone.
+template <bool SPARSE>
+constexpr int wait_next_unit() { return SPARSE ? 0x0F78 : 0x0F7C; }
+constexpr int kWaitLgkm0 = 0xC07F;
+
+__device__ __forceinline__ float partner(float x, int g) {
+  // value of lane l ^ 32
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(g ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ uint32_t partner_u(uint32_t x, int g) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return g ? r[0] : r[1];
+}
 
 }  // namespace
 
 template <bool SPARSE, int KB>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 lds_k[2][kUnit * kHeadDim];
-  __shared__ __attribute__((aligned(16))) u16 lds_v[2][kUnit * kHeadDim];
+  constexpr int kStages = stages<SPARSE>();
+  constexpr int kWaitNext = wait_next_unit<SPARSE>();
+  __shared__ __attribute__((aligned(16))) u16 lds_k[kStages][kStageElems];
+  __shared__ __attribute__((aligned(16))) u16 lds_v[kStages][kStageElems];
   __shared__ uint32_t wmask[2][4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, r32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
-  // run of (head, query tile, split) so the workgroups sharing an L2 read the
-  // same head's keys and values.
-  const int per_xcd = gridDim.x >> 3;
-  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  // Natural order: consecutive workgroups take consecutive query tiles of one
+  // head and are dealt to the 8 XCDs round-robin, so all XCDs work on the same
+  // one or two heads at a time and those heads' keys and values stay in the
+  // memory-side cache.
+  const int logical = blockIdx.x;
   if (logical >= a.total) return;
   const int split = logical % a.splits;
   const int tq = logical / a.splits;
@@ -88,54 +118,45 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     m = -__builtin_inff();
   }
 
-  // ---- staging: 64 rows x 16 chunks of K and of V, 4 + 4 chunks per thread ----
-  u32x4 stg[8];
-  // Rows past the last key re-read the last key (finite data): their scores are
-  // masked and their probabilities are zero, so no load needs a predicate.
-  auto issue_loads = [&](int key0) __attribute__((always_inline)) {
+  // The query fragment and row statistics are the only loads the compiler
+  // tracks; drain them here so that no wait it places later also waits for
+  // the key/value prefetches below (which it does not track).
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---- direct global -> LDS loads of one unit: wave w fills K and V rows
+  // 8w .. 8w+7, four rows (1 KiB) per instruction; lane l lands in chunk slot
+  // l % 16 of row l / 16 and fetches the global chunk that slot holds.
+  // Rows past the last key re-read the last key (finite data): their scores
+  // are masked and their probabilities are zero.
+  auto dma_unit = [&](int key0, int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int rep = 0; rep < 4; ++rep) {
-      const int idx = tid + 256 * rep, r = idx >> 4, c = idx & 15;
-      const int64_t off = (int64_t)min(key0 + r, Nk - 1) * kHeadDim + c * 8;
-      stg[rep] = gload<u32x4>(kh + off);
-      stg[4 + rep] = gload<u32x4>(vh + off);
-    }
-  };
-  auto write_lds = [&](int st) __attribute__((always_inline)) {
-#pragma unroll
-    for (int rep = 0; rep < 4; ++rep) {
-      const int idx = tid + 256 * rep, r = idx >> 4, c = idx & 15;
-      *reinterpret_cast<u32x4*>(&lds_k[st][k_off(r, c)]) = stg[rep];
-      *reinterpret_cast<u32x4*>(&lds_v[st][v_off(r, c)]) = stg[4 + rep];
+    for (int i = 0; i < 2; ++i) {
+      const int r0 = wave * 8 + i * 4;
+      const int r = r0 + (lane >> 4), slot = lane & 15;
+      const int64_t key = min(key0 + r, Nk - 1);
+      dma_to_lds16(kh + key * kHeadDim + (k_slot(r, slot) << 3), lds_addr(&lds_k[st][r0 * kHeadDim]));
+      dma_to_lds16(vh + key * kHeadDim + (v_slot(r, slot) << 3), lds_addr(&lds_v[st][r0 * kHeadDim]));
     }
   };
 
   // ---- exact online-softmax update with one staged unit ----
   auto compute = [&](int st, int key0, bool mine) __attribute__((always_inline)) {
-    f32x16 s[2];
+    f32x16 s = {};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = f32x16{};
-      const int r = kt * 32 + r32;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(&lds_k[st][k_off(r, ks * 2 + g)]);
-        s[kt] = mfma32(as_bf16x8(ka), qf.k[ks], s[kt]);
-      }
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(
+          &lds_k[st][r32 * kHeadDim + (k_slot(r32, ks * 2 + g) << 3)]);
+      s = mfma32(as_bf16x8(ka), qf.k[ks], s);
     }
     if (key0 + kUnit > Nk) {  // ragged last unit: keys past the end do not exist
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (key0 + kt * 32 + acc_row(i, g) >= Nk) s[kt][i] = -__builtin_inff();
+      for (int i = 0; i < 16; ++i)
+        if (key0 + acc_row(i, g) >= Nk) s[i] = -__builtin_inff();
     }
-    float mx = -__builtin_inff();
+    float mx = s[0];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, partner(mx, g));
     const float mc = mx * sl2;
     // move the reference only when the max outruns it by more than the slack
     const bool up = mine && (mc > m + kRescaleSlack);
@@ -147,177 +168,187 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     }
     if (up) m = mc;
     const float neg_ref = mine ? -m : -__builtin_inff();  // rows that did not select: p = 0
-    bf16x8 pb[4];
-    float rs = 0.f;
+    bf16x8 pb[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int i = 0; i < 16; ++i)
+      pb[i >> 3][i & 7] = (__bf16)fast_exp2(__builtin_fmaf(s[i], sl2, neg_ref));
+    // Row sum of the bf16 probabilities (the values the PV product uses), two
+    // per instruction: dot(p_pair, (1, 1)) accumulated in fp32.
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pe = fast_exp2(__builtin_fmaf(s[kt][i], sl2, neg_ref));
-        rs += pe;
-        pb[kt * 2 + (i >> 3)][i & 7] = (__bf16)pe;
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {pb[t][2 * e], pb[t][2 * e + 1]};
+        rsum[e] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rsum[e], false);
       }
-    }
-    l += rs;
-    // O^T += V^T P^T: the V^T operand of k-step (kt, h2) holds keys
-    // kt*32 + h2*16 + {4g..4g+3, 8+4g..8+4g+3} -- the keys of P that this lane
-    // half holds -- read as two transposed 4 x 16 blocks per 16-lane group.
+    l += (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
+    // O^T += V^T P^T: the V^T operand of k-step h2 holds keys
+    // h2*16 + {4g..4g+3, 8+4g..8+4g+3} -- the keys of P this lane half holds --
+    // read as two transposed 4 x 16 blocks per 16-lane group.
     const int G = lane >> 4, j = lane & 15;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int r0 = h2 * 16 + g * 4 + (j >> 2);
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int r0 = kt * 32 + h2 * 16 + g * 4 + (j >> 2);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int col = dt * 32 + (G & 1) * 16 + 4 * (j & 3);
-          const u32x2 v0 = lds_read_tr16(&lds_v[st][v_off(r0, col >> 3) + (col & 7)]);
-          const u32x2 v1 = lds_read_tr16(&lds_v[st][v_off(r0 + 8, col >> 3) + (col & 7)]);
-          const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
-          o[dt] = mfma32(as_bf16x8(va), pb[kt * 2 + h2], o[dt]);
-        }
+      for (int dt = 0; dt < 4; ++dt) {
+        const int col = dt * 32 + (G & 1) * 16 + 4 * (j & 3);
+        const u32x2 v0 = lds_read_tr16(&lds_v[st][r0 * kHeadDim + (v_slot(r0, col >> 3) << 3) + (col & 7)]);
+        const u32x2 v1 = lds_read_tr16(&lds_v[st][(r0 + 8) * kHeadDim + (v_slot(r0 + 8, col >> 3) << 3) + (col & 7)]);
+        const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
+        o[dt] = mfma32(as_bf16x8(va), pb[h2], o[dt]);
       }
     }
   };
 
-  // ---- the stream of units: key offset, and whether this row / this wave take it ----
-  struct Unit {
-    int key0;
-    bool mine, need;
-  };
-
-  if constexpr (SPARSE) {
-    const u16* khi = a.khi + (int64_t)h * a.nb_pad * kHeadDim;
-    const u16* klo = a.klo + (int64_t)h * a.nb_pad * kHeadDim;
-    const u16* vsum = a.vsumT + (int64_t)h * kHeadDim * a.nb_pad;
-    // Route one chunk of 32 blocks: proxy scores, selection, Taylor part of
-    // the rejected blocks (at the current reference m).  Returns the blocks any
-    // row of the workgroup selected; `full` = this row's, `wv` = this wave's.
-    auto route = [&](int c0, int parity, uint32_t& full, uint32_t& wv)
-        __attribute__((always_inline)) -> uint32_t {
-      const f32x16 p = proxy_chunk_hl(qf, khi, klo, c0, lane);
-      const float f = fast_exp2(mu * kLog2e - m);  // e^{mu} relative to the reference
-      uint32_t mine = 0;
-      // Weights enter the MFMA as bf16 hi + lo parts: when many blocks share
-      // nearly the same weight, a single bf16 rounding would bias the Taylor
-      // mass coherently instead of averaging out.
-      bf16x8 whi[2], wlo[2];
-      float wden = 0.f;
+  // ---- one loop: iteration t issues the loads of unit t into stage t % S and
+  // computes unit t - A (A = S - 1), issued A iterations earlier.  Unit slots
+  // shift by one per iteration, so every index is static.  Once the stream is
+  // exhausted, iterations load key 0 into a stage nobody reads (keeping the
+  // count of loads in flight exact) until the last unit is computed.
+  constexpr int A = kStages - 1;
+  int qkey[A + 1];
+  bool qmine[A + 1], qneed[A + 1], qval[A + 1];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int off = acc_row(i, g);
-        const int blk = c0 + off;
-        const bool inr = qvalid && blk < t_end;
-        const bool sel = inr && is_selected(p[i], tau);
-        mine |= (uint32_t)sel << off;
-        const float wt = (inr && !sel) ? (1.f + p[i] - mu) * f : 0.f;
-        __bf16 wh, wl;
-        split_bf16(wt, wh, wl);
-        whi[i >> 3][i & 7] = wh;
-        wlo[i >> 3][i & 7] = wl;
-        const int nj = inr ? min(KB, Nk - blk * KB) : 0;
-        wden = __builtin_fmaf((float)nj, wt, wden);
-      }
-      // Taylor part: O^T += (block sums of V)^T W^T over the chunk, on MFMA
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const u32x4 va = gload<u32x4>(vsum + (int64_t)(dt * 32 + r32) * a.nb_pad + c0 + h2 * 16 + g * 8);
-          o[dt] = mfma32(as_bf16x8(va), whi[h2], o[dt]);
-          o[dt] = mfma32(as_bf16x8(va), wlo[h2], o[dt]);
-        }
-      }
-      l += wden;
-      full = mine | __shfl_xor(mine, 32);
-      uint32_t w = full;
-#pragma unroll
-      for (int sh = 1; sh < 32; sh <<= 1) w |= __shfl_xor(w, sh);
-      wv = w;
-      if (lane == 0) wmask[parity][wave] = w;
-      __syncthreads();
-      return wmask[parity][0] | wmask[parity][1] | wmask[parity][2] | wmask[parity][3];
-    };
-
-    // chunk A is being consumed; chunk B (the next one) is already routed
-    int cA = t_begin, cB = t_begin + kChunk;
-    uint32_t fullA, wvA, fullB = 0, wvB = 0, UB = 0;
-    uint32_t UA = route(cA, 0, fullA, wvA);
-    if (cB < t_end) UB = route(cB, 1, fullB, wvB);
-    int pend = -1;  // second half of a 128-key block still to come
-    bool pend_mine = false, pend_need = false;
-    auto next = [&](Unit& u) __attribute__((always_inline)) -> bool {
-      if (KB == 128 && pend >= 0) {
-        u = Unit{pend, pend_mine, pend_need};
-        pend = -1;
-        return true;
-      }
-      while (true) {
-        if (UA) {
-          const int b = __builtin_ctz(UA);
-          UA &= UA - 1;
-          u = Unit{(cA + b) * KB, ((fullA >> b) & 1u) != 0, ((wvA >> b) & 1u) != 0};
-          if (KB == 128) {
-            pend = u.key0 + kUnit;
-            pend_mine = u.mine;
-            pend_need = u.need;
-          }
-          return true;
-        }
-        if (cB >= t_end) return false;
-        cA = cB;
-        UA = UB;
-        fullA = fullB;
-        wvA = wvB;
-        cB += kChunk;
-        UB = 0;
-        if (cB < t_end) UB = route(cB, ((cB - t_begin) / kChunk) & 1, fullB, wvB);
-      }
-    };
-
-    Unit cur, nxt;
-    bool have = next(cur);
-    int st = 0;
-    if (have) {
-      issue_loads(cur.key0);
-      write_lds(0);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // as in the dense loop: nothing outstanding at loop entry
-    __syncthreads();
-    while (have) {
-      const bool hn = next(nxt);
-      if (hn) issue_loads(nxt.key0);
-      if (cur.need) compute(st, cur.key0, cur.mine);
-      if (hn) write_lds(st ^ 1);
-      __syncthreads();
-      st ^= 1;
-      cur = nxt;
-      have = hn;
-    }
-  } else {
-    const int u_begin = t_begin * (KB / kUnit);
-    const int u_end = min(t_end * (KB / kUnit), (Nk + kUnit - 1) / kUnit);
-    int st = 0;
-    if (u_begin < u_end) {
-      issue_loads(u_begin * kUnit);
-      write_lds(0);
-    }
-    // Drain every load issued so far (query fragment included) on all paths, so
-    // the loop's only outstanding loads are the prefetches its LDS writes wait for.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int u = u_begin; u < u_end; ++u) {
-      const bool hn = u + 1 < u_end;
-      if (hn) issue_loads((u + 1) * kUnit);
-      compute(st, u * kUnit, true);
-      if (hn) write_lds(st ^ 1);
-      __syncthreads();
-      st ^= 1;
-    }
+  for (int i = 0; i <= A; ++i) {
+    qkey[i] = 0;
+    qmine[i] = qneed[i] = qval[i] = false;
   }
+  int st_issue = 0;
+  bool stream_done = false;
+
+  // unit sources
+  int u_next = t_begin * (KB / kUnit);                                 // dense
+  const int u_end = min(t_end * (KB / kUnit), (Nk + kUnit - 1) / kUnit);
+  int c_next = t_begin, cA = 0, parity = 0;                            // sparse
+  uint32_t UA = 0, fullA = 0, wvA = 0;
+  int pend_left = 0, pend_key = 0;
+  bool pend_mine = false, pend_need = false;
+  const u16* khi = SPARSE ? a.khi + (int64_t)h * a.nb_pad * kHeadDim : nullptr;
+  const u16* klo = SPARSE ? a.klo + (int64_t)h * a.nb_pad * kHeadDim : nullptr;
+  const u16* vsum = SPARSE ? a.vsumT + (int64_t)h * kHeadDim * a.nb_pad : nullptr;
+
+  while (true) {
+    // -- next unit of the stream --
+    bool have = false;
+    int key0 = 0;
+    bool mi = false, ne = false;
+    if (!stream_done) {
+      if constexpr (SPARSE) {
+        if (pend_left == 0) {
+          // Route chunks of 32 blocks until one has a selected block: proxy
+          // scores, selection, and the Taylor part of the rejected blocks (at
+          // the current reference m).  Any row of the workgroup selecting a
+          // block makes the block a unit source; `fullA` = this row's
+          // selections, `wvA` = this wave's.
+          while (UA == 0 && c_next < t_end) {
+            const int c0 = c_next;
+            const f32x16 p = proxy_chunk_hl(qf, khi, klo, c0, lane);
+            const float f = fast_exp2(mu * kLog2e - m);  // e^{mu} relative to the reference
+            uint32_t sel_bits = 0;
+            // Weights enter the MFMA as bf16 hi + lo parts: when many blocks
+            // share nearly the same weight, a single bf16 rounding would bias
+            // the Taylor mass coherently instead of averaging out.
+            bf16x8 whi[2], wlo[2];
+            float wden = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int off = acc_row(i, g);
+              const int blk = c0 + off;
+              const bool inr = qvalid && blk < t_end;
+              const bool sel = inr && is_selected(p[i], tau);
+              sel_bits |= (uint32_t)sel << off;
+              const float wt = (inr && !sel) ? (1.f + p[i] - mu) * f : 0.f;
+              __bf16 wh, wl;
+              split_bf16(wt, wh, wl);
+              whi[i >> 3][i & 7] = wh;
+              wlo[i >> 3][i & 7] = wl;
+              const int nj = inr ? min(KB, Nk - blk * KB) : 0;
+              wden = __builtin_fmaf((float)nj, wt, wden);
+            }
+            // Taylor part: O^T += (block sums of V)^T W^T over the chunk, on MFMA
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+              for (int dt = 0; dt < 4; ++dt) {
+                const u32x4 va =
+                    gload<u32x4>(vsum + (int64_t)(dt * 32 + r32) * a.nb_pad + c0 + h2 * 16 + g * 8);
+                o[dt] = mfma32(as_bf16x8(va), whi[h2], o[dt]);
+                o[dt] = mfma32(as_bf16x8(va), wlo[h2], o[dt]);
+              }
+            }
+            l += wden;
+            fullA = sel_bits | partner_u(sel_bits, g);
+            uint32_t w = fullA;
+#pragma unroll
+            for (int sh = 1; sh < 32; sh <<= 1) w |= __shfl_xor(w, sh);
+            wvA = w;
+            if (lane == 0) wmask[parity][wave] = w;
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            __builtin_amdgcn_s_barrier();
+            UA = wmask[parity][0] | wmask[parity][1] | wmask[parity][2] | wmask[parity][3];
+            cA = c0;
+            c_next += kChunk;
+            parity ^= 1;
+          }
+          if (UA) {
+            const int b = __builtin_ctz(UA);
+            UA &= UA - 1;
+            pend_key = (cA + b) * KB;
+            pend_left = KB / kUnit;
+            pend_mine = ((fullA >> b) & 1u) != 0;
+            pend_need = ((wvA >> b) & 1u) != 0;
+          }
+        }
+        if (pend_left > 0) {
+          have = true;
+          key0 = pend_key;
+          mi = pend_mine;
+          ne = pend_need;
+          pend_key += kUnit;
+          --pend_left;
+        }
+      } else {
+        if (u_next < u_end) {
+          have = true;
+          key0 = u_next * kUnit;
+          mi = ne = true;
+          ++u_next;
+        }
+      }
+      stream_done = !have;
+    }
+    bool pending = false;  // units issued but not yet computed
+#pragma unroll
+    for (int i = 1; i <= A; ++i) pending |= qval[i];
+    if (stream_done && !pending) break;
+
+    // -- issue unit t, shift the slots, compute unit t - A --
+    dma_unit(key0, st_issue);
+#pragma unroll
+    for (int i = 0; i < A; ++i) {
+      qkey[i] = qkey[i + 1];
+      qmine[i] = qmine[i + 1];
+      qneed[i] = qneed[i + 1];
+      qval[i] = qval[i + 1];
+    }
+    qkey[A] = key0;
+    qmine[A] = mi;
+    qneed[A] = ne;
+    qval[A] = have;
+    const int st_comp = st_issue == kStages - 1 ? 0 : st_issue + 1;
+    st_issue = st_comp;
+    if (qval[0] && qneed[0]) compute(st_comp, qkey[0], qmine[0]);
+    __builtin_amdgcn_s_waitcnt(kWaitNext);  // this wave's loads of the next unit landed
+    __builtin_amdgcn_s_barrier();           // ... and every wave's; its stage is free to refill
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
 
   // ---- epilogue ----
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = l + partner(l, g);
   if (!qvalid) return;
   if (a.splits == 1) {
     const float inv = 1.f / lt;

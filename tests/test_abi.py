@@ -95,7 +95,7 @@ def test_workspace_sizes(lib):
     nb = (N + B - 1) // B
     s = ws(N, N, H, 128, B, 1)
     assert s >= 2 * H * nb * 128 * 4 + 2 * H * N * 4
-    assert s < 80 * 2 ** 20
+    assert s < 128 * 2 ** 20  # pooled K/V, bf16 copies, mu, sigma: ~92 MB at 4K
     assert s < H * N * nb  # far below one byte per proxy score
     # dense self-attention at large N needs no workspace
     assert ws(N, N, H, 128, B, 0) == 0
