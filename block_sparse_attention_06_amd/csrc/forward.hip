@@ -43,17 +43,20 @@ constexpr float kRescaleSlack = 8.f;             // log2 units the reference may
 __device__ __forceinline__ int k_slot(int row, int c) { return c ^ (row & 15); }
 __device__ __forceinline__ int v_slot(int row, int c) { return c ^ ((row & 3) << 2); }
 
-// LDS ring depth: two workgroups per CU share 160 KiB.  Dense mode uses five
-// 16 KiB stages (loads four units ahead); sparse mode needs a few bytes for the
-// routing masks and uses four (three units ahead).
-template <bool SPARSE>
-constexpr int stages() { return SPARSE ? 4 : 5; }
+// LDS ring depth.  Four-wave workgroups run two per CU and share 160 KiB:
+// five 16 KiB stages each (loads four units ahead).  Eight-wave workgroups run
+// one per CU and use eight stages (seven units ahead).
+template <bool SPARSE, int WAVES>
+constexpr int stages() { return WAVES == 8 ? 8 : 5; }
 
-// s_waitcnt immediates (gfx9 encoding): vmcnt(4 x (stages - 2)) -- this wave's
-// loads of the next unit done while the later units' stay in flight -- and
-// lgkmcnt(0) alone.
-template <bool SPARSE>
-constexpr int wait_next_unit() { return SPARSE ? 0x0F78 : 0x0F7C; }
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(n) alone.
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// Each wave issues 16 / WAVES loads per unit; waiting until only the loads of
+// the stages - 2 later units are in flight means this wave's loads of the next
+// unit have landed.
+template <bool SPARSE, int WAVES>
+constexpr int wait_next_unit() { return vm_wait((16 / WAVES) * (stages<SPARSE, WAVES>() - 2)); }
 constexpr int kWaitLgkm0 = 0xC07F;
 
 __device__ __forceinline__ float partner(float x, int g) {
@@ -69,13 +72,13 @@ __device__ __forceinline__ uint32_t partner_u(uint32_t x, int g) {
 
 }  // namespace
 
-template <bool SPARSE, int KB>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
-  constexpr int kStages = stages<SPARSE>();
-  constexpr int kWaitNext = wait_next_unit<SPARSE>();
+template <bool SPARSE, int KB, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 2) void fwd_kernel(FwdArgs a) {
+  constexpr int kStages = stages<SPARSE, WAVES>();
+  constexpr int kWaitNext = wait_next_unit<SPARSE, WAVES>();
+  constexpr int kRowsPerWave = kUnit / WAVES;  // unit rows each wave loads
   __shared__ __attribute__((aligned(16))) u16 lds_k[kStages][kStageElems];
   __shared__ __attribute__((aligned(16))) u16 lds_v[kStages][kStageElems];
-  __shared__ uint32_t wmask[2][4];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int split = logical % a.splits;
   const int tq = logical / a.splits;
   const int qt = tq % a.n_qt, h = tq / a.n_qt;
-  const int row = qt * kQTile + wave * 32 + r32;
+  const int row = qt * (32 * WAVES) + wave * 32 + r32;
   const bool qvalid = row < a.N;
 
   QFrag qf;
@@ -124,14 +127,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
 
   // ---- direct global -> LDS loads of one unit: wave w fills K and V rows
-  // 8w .. 8w+7, four rows (1 KiB) per instruction; lane l lands in chunk slot
+  // w*32/WAVES onwards, four rows (1 KiB) per instruction; lane l lands in chunk slot
   // l % 16 of row l / 16 and fetches the global chunk that slot holds.
   // Rows past the last key re-read the last key (finite data): their scores
   // are masked and their probabilities are zero.
   auto dma_unit = [&](int key0, int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r0 = wave * 8 + i * 4;
+    for (int i = 0; i < kRowsPerWave / 4; ++i) {
+      const int r0 = wave * kRowsPerWave + i * 4;
       const int r = r0 + (lane >> 4), slot = lane & 15;
       const int64_t key = min(key0 + r, Nk - 1);
       dma_to_lds16(kh + key * kHeadDim + (k_slot(r, slot) << 3), lds_addr(&lds_k[st][r0 * kHeadDim]));
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   // unit sources
   int u_next = t_begin * (KB / kUnit);                                 // dense
   const int u_end = min(t_end * (KB / kUnit), (Nk + kUnit - 1) / kUnit);
-  int c_next = t_begin, cA = 0, parity = 0;                            // sparse
+  int c_next = t_begin, cA = 0;                                        // sparse
   uint32_t UA = 0, fullA = 0, wvA = 0;
   int pend_left = 0, pend_key = 0;
   bool pend_mine = false, pend_need = false;
@@ -286,13 +289,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int sh = 1; sh < 32; sh <<= 1) w |= __shfl_xor(w, sh);
             wvA = w;
-            if (lane == 0) wmask[parity][wave] = w;
+            // Exchange the wave masks through the last bytes of the K tile of
+            // the stage about to be refilled: nothing reads it until the unit
+            // issued next lands, and the second barrier keeps every read of the
+            // masks ahead of that refill.
+            uint32_t* wmask = reinterpret_cast<uint32_t*>(&lds_k[st_issue][kStageElems - 2 * WAVES]);
+            if (lane == 0) wmask[wave] = w;
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
             __builtin_amdgcn_s_barrier();
-            UA = wmask[parity][0] | wmask[parity][1] | wmask[parity][2] | wmask[parity][3];
+            uint32_t un = 0;
+#pragma unroll
+            for (int i = 0; i < WAVES; ++i) un |= wmask[i];
+            UA = un;
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            __builtin_amdgcn_s_barrier();
             cA = c0;
             c_next += kChunk;
-            parity ^= 1;
           }
           if (UA) {
             const int b = __builtin_ctz(UA);
@@ -387,11 +399,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 hipError_t launch_forward(const FwdArgs& a, bool sparse, int B, hipStream_t s) {
   const int grid = (a.total + 7) & ~7;
   if (!sparse)
-    fwd_kernel<false, 128><<<grid, 256, 0, s>>>(a);
+    fwd_kernel<false, 128, 4><<<grid, 256, 0, s>>>(a);
   else if (B == 64)
-    fwd_kernel<true, 64><<<grid, 256, 0, s>>>(a);
+    fwd_kernel<true, 64, 4><<<grid, 256, 0, s>>>(a);
   else
-    fwd_kernel<true, 128><<<grid, 256, 0, s>>>(a);
+    fwd_kernel<true, 128, 4><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -59,7 +59,7 @@ struct FwdArgs {
   float beta;
   int N, Nk, H;
   int nb, nb_pad;      // key tiles (sparse: blocks of B) and padded count
-  int n_qt;            // query tiles of 128 rows
+  int n_qt;            // query tiles (32 rows per wave)
   int splits, tiles_per_split;
   int total;           // H * n_qt * splits
 };
