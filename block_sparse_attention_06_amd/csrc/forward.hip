@@ -396,14 +396,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_kernel(FwdArgs a) {
   }
 }
 
+// Dense attention only: the sparse path runs fwd4_kernel.
 hipError_t launch_forward(const FwdArgs& a, bool sparse, int B, hipStream_t s) {
+  (void)B;
+  if (sparse) return hipErrorInvalidValue;
   const int grid = (a.total + 7) & ~7;
-  if (!sparse)
-    fwd_kernel<false, 128, 4><<<grid, 256, 0, s>>>(a);
-  else if (B == 64)
-    fwd_kernel<true, 64, 4><<<grid, 256, 0, s>>>(a);
-  else
-    fwd_kernel<true, 128, 4><<<grid, 256, 0, s>>>(a);
+  fwd_kernel<false, 128, 4><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,467 @@
+// Fused attention forward for gfx950 with a pipelined key loop: dense softmax
+// attention, and query-thresholded block-sparse attention with a first-order
+// Taylor term for the rejected blocks, in one online-softmax pass.
+//
+// Sol-Engine LTX25 page, "Stage 2 Optimization -- Core Technology: Sol-Attn":
+//  - routing is folded into the softmax pass: pooled keys are taken 32 blocks
+//    at a time ("chunk-wise"), their proxy scores are compared with each row's
+//    threshold, and only the selected blocks' key/value tiles are fetched --
+//    the proxy scores of a chunk live in registers and are never stored;
+//  - rejected blocks contribute n_j e^{mu_i} (1 + p_ij - mu_i) on the pooled
+//    value (numerator) and the same weight (denominator).
+// doubleAI page, "Attention across two GPUs": with few query tiles the key
+// range is split over workgroups and the partial answers, each carrying its
+// running maximum and denominator, are merged exactly (combine_kernel).
+//
+// Workgroup: 4 waves x 32 query rows = 128 rows of one head; two workgroups
+// per CU.  Keys stream through LDS in units of 32 rows of K and V, in a ring of
+// five stages filled by direct global->LDS loads.  A load takes a scalar base
+// (the unit's first key) and a per-lane offset fixed for the whole kernel, so
+// issuing a unit costs no vector arithmetic.
+//
+// Per iteration each wave (1) runs the online softmax of the oldest unit in
+// flight on its S tile, computed one iteration earlier, (2) routes and issues
+// the loads of the newest unit, (3) issues the S^T = K Q^T products of the next
+// unit, and (4) issues O^T += V^T P^T for the oldest unit.  The softmax therefore never
+// waits for its own products, and the matrix products of (3) and (4) run while
+// the wave crosses the barrier and starts the next softmax.  Each wave then
+// waits only for its own loads of the unit whose S comes next, and one barrier
+// per unit publishes them and frees the stage refilled next.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace solattn {
+
+namespace {
+
+constexpr int kU = 32;                  // keys per staged unit
+constexpr int kUE = kU * kHeadDim;      // bf16 per tensor per stage
+constexpr int kRing = 5;                // LDS stages (80 KiB: two workgroups per CU)
+constexpr int kAhead = kRing - 1;       // units in flight beyond the one whose PV runs
+constexpr int kDmaPerUnit = 4;          // loads per wave per unit: 2 groups of 4 rows, K and V
+constexpr float kSlack = 8.f;           // log2 units the reference may lag the row max
+constexpr int kLgkm0 = 0xC07F;          // s_waitcnt lgkmcnt(0)
+
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(n) alone.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+// At the end of an iteration the loads of the next two units (S next, PV
+// after) must have landed; the kAhead - 2 younger units may still be in flight.
+constexpr int kWaitNext = vmcnt_imm(kDmaPerUnit * (kAhead - 2));
+
+// LDS layouts of a unit ([32 rows][128 bf16], 16-byte chunks): K rows put
+// chunk c at c ^ (row % 16), so the S operand reads 16 consecutive rows at one
+// chunk without bank conflicts; V rows put chunk c at c ^ 4 (row % 4), so the
+// transposing read of 4 consecutive rows x 4 chunks per 16 lanes is
+// conflict-free.
+__device__ __forceinline__ int kslot(int row, int c) { return c ^ (row & 15); }
+__device__ __forceinline__ int vslot(int row, int c) { return c ^ ((row & 3) << 2); }
+
+// Direct global -> LDS load of 16 bytes per lane from sbase + voff (sbase
+// wave-uniform, voff a 32-bit per-lane byte offset); lane l's bytes land at LDS
+// byte address lds + 16 l.  Inline assembly keeps the compiler from treating
+// it as a pending write to all of LDS; the caller orders it with explicit
+// vector-memory waits and barriers.
+__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ float partner_f(float x, int g) {
+  // value of lane l ^ 32
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(g ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ uint32_t partner_b(uint32_t x, int g) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return g ? r[0] : r[1];
+}
+
+// Workgroup barrier that is also a compiler barrier for memory accesses (the
+// hardware barrier alone does not stop the compiler from moving LDS reads).
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+}  // namespace
+
+template <bool SPARSE, int KB>
+__global__ __launch_bounds__(256, 2) void fwd4_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 lds_k[kRing][kUE];
+  __shared__ __attribute__((aligned(16))) u16 lds_v[kRing][kUE];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // Natural order: consecutive workgroups take consecutive query tiles of one
+  // head and are dealt to the 8 XCDs round-robin, so all XCDs work on the same
+  // one or two heads at a time.
+  const int logical = blockIdx.x;
+  if (logical >= a.total) return;
+  const int split = logical % a.splits;
+  const int tq = logical / a.splits;
+  const int qt = tq % a.n_qt, h = tq / a.n_qt;
+  const int row = qt * kQTile + wave * 32 + r32;
+  const bool qvalid = row < a.N;
+
+  QFrag qf;
+  load_qfrag(qf, a.q + (int64_t)h * a.N * kHeadDim, row, qvalid, g);
+  const u16* kh = a.k + (int64_t)h * a.Nk * kHeadDim;
+  const u16* vh = a.v + (int64_t)h * a.Nk * kHeadDim;
+  const int Nk = a.Nk;
+
+  const int t_begin = split * a.tiles_per_split;
+  const int t_end = min(a.nb, t_begin + a.tiles_per_split);
+  const float sl2 = 0.08838834764831845f * kLog2e;  // softmax scale in log2 units
+
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+  float l = 0.f;  // this lane's share of the denominator, relative to 2^m
+  float m;        // reference of the running sums (log2 units), within kSlack of the max
+  float mu = 0.f, tau = __builtin_inff();
+  if constexpr (SPARSE) {
+    if (qvalid) {
+      mu = gload<float>(a.mu + (int64_t)h * a.N + row);
+      tau = make_tau(mu, gload<float>(a.sigma + (int64_t)h * a.N + row), a.beta);
+    }
+    m = mu * kLog2e;  // Taylor terms are relative to e^mu: start the reference there
+  } else {
+    m = -__builtin_inff();
+  }
+
+  // The query fragment and row statistics are the only loads the compiler
+  // tracks; drain them here so that no wait it places later also waits for
+  // the key/value loads below (which it does not track).
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---- direct loads of one unit: wave w fills K and V rows 8w .. 8w+7 in two
+  // groups of four rows (1 KiB per instruction); lane l lands in chunk slot
+  // l % 16 of row l / 16 of its group and fetches the global chunk that slot
+  // holds.  Offsets are relative to the unit's first key.
+  const int slot = lane & 15;
+  uint32_t offk[2], offv[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = wave * 8 + i * 4 + (lane >> 4);
+    offk[i] = (uint32_t)(r * kHeadDim + (kslot(r, slot) << 3)) * 2u;
+    offv[i] = (uint32_t)(r * kHeadDim + (vslot(r, slot) << 3)) * 2u;
+  }
+  // Every unit of the stream starts at a key < Nk (key 0 for the stream past
+  // its end); the clamp below keeps even a violation of that inside the buffer.
+  auto dma_unit = [&](int key0, int st) __attribute__((always_inline)) {
+    key0 = min(__builtin_amdgcn_readfirstlane(key0), Nk - 1);
+    st = __builtin_amdgcn_readfirstlane(st);
+    const u16* kb = kh + (int64_t)key0 * kHeadDim;
+    const u16* vb = vh + (int64_t)key0 * kHeadDim;
+    if (key0 + kU <= Nk) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r0 = wave * 8 + i * 4;
+        dma16_sv(kb, offk[i], lds_addr(&lds_k[st][r0 * kHeadDim]));
+        dma16_sv(vb, offv[i], lds_addr(&lds_v[st][r0 * kHeadDim]));
+      }
+    } else {
+      // ragged last unit: rows past the last key re-read the last key (finite
+      // data); their scores are masked and their probabilities are zero
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r0 = wave * 8 + i * 4;
+        const int r = r0 + (lane >> 4);
+        const int rr = min(r, Nk - 1 - key0);
+        const uint32_t ok = (uint32_t)(rr * kHeadDim + (kslot(r, slot) << 3)) * 2u;
+        const uint32_t ov = (uint32_t)(rr * kHeadDim + (vslot(r, slot) << 3)) * 2u;
+        dma16_sv(kb, ok, lds_addr(&lds_k[st][r0 * kHeadDim]));
+        dma16_sv(vb, ov, lds_addr(&lds_v[st][r0 * kHeadDim]));
+      }
+    }
+  };
+
+  // ---- S^T = K Q^T of one staged unit (issued only; consumed an iteration later)
+  auto mma_s = [&](int st) __attribute__((always_inline)) {
+    f32x16 s = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(
+          &lds_k[st][r32 * kHeadDim + (kslot(r32, ks * 2 + g) << 3)]);
+      s = mfma32(as_bf16x8(ka), qf.k[ks], s);
+    }
+    return s;
+  };
+
+  // ---- online softmax of one unit's S tile: probabilities as the bf16 B
+  // operand of the PV product (keys permuted within 16 as the accumulator
+  // layout holds them), row sums into l, reference moves into m / o / l.
+  auto softmax = [&](f32x16 s, int key0, bool mine, bf16x8 (&pb)[2]) __attribute__((always_inline)) {
+    if (key0 + kU > Nk) {  // ragged last unit: keys past the end do not exist
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (key0 + acc_row(i, g) >= Nk) s[i] = -__builtin_inff();
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, partner_f(mx, g));
+    const float mc = mx * sl2;
+    // move the reference only when the max outruns it by more than the slack
+    const bool up = mine && (mc > m + kSlack);
+    if (__ballot(up)) {
+      const float alpha = up ? fast_exp2(m - mc) : 1.f;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+    }
+    if (up) m = mc;
+    const float neg_ref = mine ? -m : -__builtin_inff();  // rows that did not select: p = 0
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      pb[i >> 3][i & 7] = (__bf16)fast_exp2(__builtin_fmaf(s[i], sl2, neg_ref));
+    // Row sum of the bf16 probabilities (the values the PV product uses), two
+    // per instruction: dot(p_pair, (1, 1)) accumulated in fp32.
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2 p0 = {pb[0][2 * e], pb[0][2 * e + 1]};
+      const bf16x2 p1 = {pb[1][2 * e], pb[1][2 * e + 1]};
+      rs0 = __builtin_amdgcn_fdot2_f32_bf16(p0, one2, rs0, false);
+      rs1 = __builtin_amdgcn_fdot2_f32_bf16(p1, one2, rs1, false);
+    }
+    l += rs0 + rs1;
+  };
+
+  // ---- O^T += V^T P^T: the V^T operand of k-step h2 holds keys
+  // h2*16 + {4g..4g+3, 8+4g..8+4g+3} -- the keys of P this lane half holds --
+  // read as two transposed 4 x 16 blocks per 16-lane group.
+  auto mma_pv = [&](int st, const bf16x8 (&pb)[2]) __attribute__((always_inline)) {
+    const int G = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int r0 = h2 * 16 + g * 4 + (j >> 2);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int col = dt * 32 + (G & 1) * 16 + 4 * (j & 3);
+        const u32x2 v0 = lds_read_tr16(&lds_v[st][r0 * kHeadDim + (vslot(r0, col >> 3) << 3) + (col & 7)]);
+        const u32x2 v1 =
+            lds_read_tr16(&lds_v[st][(r0 + 8) * kHeadDim + (vslot(r0 + 8, col >> 3) << 3) + (col & 7)]);
+        const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
+        o[dt] = mfma32(as_bf16x8(va), pb[h2], o[dt]);
+      }
+    }
+  };
+
+  // ---- unit queue.  After the shift of iteration i, slot j holds unit
+  // i - kAhead + j: slot 0 gets its softmax and PV, slot 1 its S, slot kAhead
+  // was just issued.  Validity / need are wave-uniform bit masks, "mine" (this
+  // row selected the unit's block) a per-lane bit mask; bit j = slot j.
+  int qkey[kAhead + 1];
+#pragma unroll
+  for (int i = 0; i <= kAhead; ++i) qkey[i] = 0;
+  uint32_t qneed = 0, qval = 0, qmine = 0;
+  int st_issue = 0;
+  bool stream_done = false;
+  f32x16 s_cur = {};  // S tile of the unit in slot 1 (before the shift), computed one iteration earlier
+
+  // unit sources
+  int u_next = t_begin * (KB / kU);                                  // dense
+  const int u_end = min(t_end * (KB / kU), (Nk + kU - 1) / kU);
+  int c_next = t_begin, cA = 0;                                      // sparse
+  uint32_t UA = 0, fullA = 0, wvA = 0;
+  int pend_left = 0, pend_key = 0;
+  bool pend_mine = false, pend_need = false;
+  const u16* khi = SPARSE ? a.khi + (int64_t)h * a.nb_pad * kHeadDim : nullptr;
+  const u16* klo = SPARSE ? a.klo + (int64_t)h * a.nb_pad * kHeadDim : nullptr;
+  const u16* vsum = SPARSE ? a.vsumT + (int64_t)h * kHeadDim * a.nb_pad : nullptr;
+
+  while (true) {
+    // -- softmax of the unit whose PV runs in this iteration (slot 1 before the
+    // shift below); done first so that only its bf16 probabilities, not its S
+    // tile, stay live through routing --
+    bf16x8 pb[2];
+    const bool pv = (qneed & 2u) != 0;
+    if (pv) softmax(s_cur, qkey[1], (qmine & 2u) != 0, pb);
+    // The tile is dead until the S product below overwrites it; saying so
+    // keeps its registers free through routing.
+    s_cur = __builtin_nondeterministic_value(s_cur);
+
+    // -- next unit of the stream --
+    bool have = false;
+    int key0 = 0;
+    bool mi = false, ne = false;
+    if (!stream_done) {
+      if constexpr (SPARSE) {
+        if (pend_left == 0) {
+          // Route chunks of 32 blocks until one has a selected block: proxy
+          // scores, selection, and the Taylor part of the rejected blocks (at
+          // the current reference m).  Any row of the workgroup selecting a
+          // block makes the block a unit source; `fullA` = this row's
+          // selections, `wvA` = this wave's.
+          while (UA == 0 && c_next < t_end) {
+            const int c0 = c_next;
+            const f32x16 p = proxy_chunk_hl(qf, khi, klo, c0, lane);
+            const float f = fast_exp2(mu * kLog2e - m);  // e^{mu} relative to the reference
+            uint32_t sel_bits = 0;
+            // Weights enter the MFMA as bf16 hi + lo parts: when many blocks
+            // share nearly the same weight, a single bf16 rounding would bias
+            // the Taylor mass coherently instead of averaging out.
+            bf16x8 whi[2], wlo[2];
+            float wden = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int off = acc_row(i, g);
+              const int blk = c0 + off;
+              const bool inr = qvalid && blk < t_end;
+              const bool sel = inr && is_selected(p[i], tau);
+              sel_bits |= (uint32_t)sel << off;
+              const float wt = (inr && !sel) ? (1.f + p[i] - mu) * f : 0.f;
+              __bf16 wh, wl;
+              split_bf16(wt, wh, wl);
+              whi[i >> 3][i & 7] = wh;
+              wlo[i >> 3][i & 7] = wl;
+              const int nj = inr ? min(KB, Nk - blk * KB) : 0;
+              wden = __builtin_fmaf((float)nj, wt, wden);
+            }
+            // Taylor part: O^T += (block sums of V)^T W^T over the chunk, on MFMA
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+              for (int dt = 0; dt < 4; ++dt) {
+                const u32x4 va =
+                    gload<u32x4>(vsum + (int64_t)(dt * 32 + r32) * a.nb_pad + c0 + h2 * 16 + g * 8);
+                o[dt] = mfma32(as_bf16x8(va), whi[h2], o[dt]);
+                o[dt] = mfma32(as_bf16x8(va), wlo[h2], o[dt]);
+              }
+            }
+            l += wden;
+            fullA = sel_bits | partner_b(sel_bits, g);
+            uint32_t w = fullA;
+#pragma unroll
+            for (int sh = 1; sh < 32; sh <<= 1) w |= __shfl_xor(w, sh);
+            w = __builtin_amdgcn_readfirstlane(w);  // equal in all lanes: make it scalar
+            wvA = w;
+            // Exchange the wave masks through the last bytes of the K tile of
+            // the stage about to be refilled: nothing reads that stage until
+            // the unit issued next lands, and the second barrier keeps every
+            // read of the masks ahead of that refill.
+            uint32_t* wmask = reinterpret_cast<uint32_t*>(&lds_k[st_issue][kUE - 8]);
+            if (lane == 0) wmask[wave] = w;
+            __builtin_amdgcn_s_waitcnt(kLgkm0);
+            wg_barrier();
+            uint32_t un = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) un |= wmask[i];
+            UA = __builtin_amdgcn_readfirstlane(un);
+            __builtin_amdgcn_s_waitcnt(kLgkm0);
+            wg_barrier();
+            cA = c0;
+            c_next += kChunk;
+          }
+          if (UA) {
+            const int b = __builtin_ctz(UA);
+            UA &= UA - 1;
+            pend_key = (cA + b) * KB;
+            // units of the block that hold at least one key (the last block
+            // may be ragged)
+            pend_left = min(KB / kU, (Nk - pend_key + kU - 1) / kU);
+            pend_mine = ((fullA >> b) & 1u) != 0;
+            pend_need = ((wvA >> b) & 1u) != 0;
+          }
+        }
+        if (pend_left > 0) {
+          have = true;
+          key0 = pend_key;
+          mi = pend_mine;
+          ne = pend_need;
+          pend_key += kU;
+          --pend_left;
+        }
+      } else {
+        if (u_next < u_end) {
+          have = true;
+          key0 = u_next * kU;
+          mi = ne = true;
+          ++u_next;
+        }
+      }
+      stream_done = !have;
+    }
+    // -- issue the newest unit (a stream past its end reloads key 0 into a
+    // stage nobody reads, so the count of loads in flight stays exact) --
+    dma_unit(key0, st_issue);
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) qkey[i] = qkey[i + 1];
+    qkey[kAhead] = key0;
+    qval = (qval >> 1) | ((uint32_t)have << kAhead);
+    qneed = (qneed >> 1) | ((uint32_t)(have && ne) << kAhead);
+    qmine = (qmine >> 1) | ((uint32_t)(have && mi) << kAhead);
+    // slot j sits in stage (st_issue + 1 + j) mod kRing
+    const int st0 = st_issue == kRing - 1 ? 0 : st_issue + 1;
+    const int st1 = st0 == kRing - 1 ? 0 : st0 + 1;
+
+    if (qneed & 2u)
+      s_cur = mma_s(st1);
+    else
+      asm volatile("" : "=v"(s_cur));  // unused: defined without an instruction
+    if (pv) mma_pv(st0, pb);
+    st_issue = st0;  // slot 0's stage is refilled next, after the barrier
+    __builtin_amdgcn_s_waitcnt(kWaitNext);  // this wave's loads of slots 1 and 2 landed
+    wg_barrier();                           // ... and every wave's
+    // done when the stream is exhausted and no issued unit awaits its PV
+    if (stream_done && (qval >> 1) == 0) break;
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
+
+  // ---- epilogue ----
+  const float lt = l + partner_f(l, g);
+  if (!qvalid) return;
+  if (a.splits == 1) {
+    const float inv = 1.f / lt;
+    u16* orow = a.out + ((int64_t)h * a.N + row) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        u32x2 pk;
+        pk[0] = (uint32_t)f32_to_bf16_bits(o[dt][q4 * 4 + 0] * inv) |
+                ((uint32_t)f32_to_bf16_bits(o[dt][q4 * 4 + 1] * inv) << 16);
+        pk[1] = (uint32_t)f32_to_bf16_bits(o[dt][q4 * 4 + 2] * inv) |
+                ((uint32_t)f32_to_bf16_bits(o[dt][q4 * 4 + 3] * inv) << 16);
+        *reinterpret_cast<u32x2*>(orow + dt * 32 + q4 * 8 + g * 4) = pk;
+      }
+    }
+    if (a.lse && g == 0) a.lse[(int64_t)h * a.N + row] = m * kLn2 + logf(lt);
+  } else {
+    const int64_t prow = ((int64_t)split * a.H + h) * a.N + row;
+    float* po = a.part_o + prow * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 v4 = {o[dt][q4 * 4], o[dt][q4 * 4 + 1], o[dt][q4 * 4 + 2], o[dt][q4 * 4 + 3]};
+        *reinterpret_cast<f32x4*>(po + dt * 32 + q4 * 8 + g * 4) = v4;
+      }
+    }
+    if (g == 0) {
+      a.part_ml[prow * 2] = m;
+      a.part_ml[prow * 2 + 1] = lt;
+    }
+  }
+}
+
+hipError_t launch_forward4(const FwdArgs& a, bool sparse, int B, hipStream_t s) {
+  const int grid = (a.total + 7) & ~7;
+  if (!sparse)
+    fwd4_kernel<false, 128><<<grid, 256, 0, s>>>(a);
+  else if (B == 64)
+    fwd4_kernel<true, 64><<<grid, 256, 0, s>>>(a);
+  else
+    fwd4_kernel<true, 128><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace solattn
