@@ -94,6 +94,7 @@ __global__ __launch_bounds__(256, 2) void fwd4_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) u16 lds_v[kRing][kUE];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+  const int g4 = g * 4;  // accumulator element i of lane half g is row acc_row(i, 0) + g4
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // Natural order: consecutive workgroups take consecutive query tiles of one
@@ -180,26 +181,36 @@ __global__ __launch_bounds__(256, 2) void fwd4_kernel(FwdArgs a) {
     }
   };
 
-  // ---- S^T = K Q^T of one staged unit (issued only; consumed an iteration later)
-  auto mma_s = [&](int st) __attribute__((always_inline)) {
+  // ---- S^T = K Q^T of one staged unit (consumed an iteration later): operand
+  // reads and products separately, so the products can be interleaved with
+  // other work.
+  auto read_k = [&](int st, u32x4 (&kf)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      kf[ks] = *reinterpret_cast<const u32x4*>(&lds_k[st][r32 * kHeadDim + (kslot(r32, ks * 2 + g) << 3)]);
+  };
+  auto mfma_s = [&](const u32x4 (&kf)[8]) __attribute__((always_inline)) {
     f32x16 s = {};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(
-          &lds_k[st][r32 * kHeadDim + (kslot(r32, ks * 2 + g) << 3)]);
-      s = mfma32(as_bf16x8(ka), qf.k[ks], s);
-    }
+    for (int ks = 0; ks < 8; ++ks) s = mfma32(as_bf16x8(kf[ks]), qf.k[ks], s);
     return s;
   };
 
-  // ---- online softmax of one unit's S tile: probabilities as the bf16 B
-  // operand of the PV product (keys permuted within 16 as the accumulator
-  // layout holds them), row sums into l, reference moves into m / o / l.
-  auto softmax = [&](f32x16 s, int key0, bool mine, bf16x8 (&pb)[2]) __attribute__((always_inline)) {
+  // ---- online softmax of one unit's S tile, in two parts.  The head masks
+  // keys past the end, finds the row max and moves the reference (m, with o
+  // and l rescaled) when the max outruns it; it returns the exponent offset
+  // (-m, or -inf for rows that did not select the unit: p = 0).  The tail
+  // forms the probabilities as the bf16 B operand of the PV product (keys
+  // permuted within 16 as the accumulator layout holds them) and adds their
+  // row sums to l.
+  auto softmax_head = [&](f32x16& s, int key0, bool mine) __attribute__((always_inline)) {
     if (key0 + kU > Nk) {  // ragged last unit: keys past the end do not exist
+      // element i holds key offset acc_row(i, 0) + 4g: compare the one
+      // per-lane term with scalar limits (no per-element lane offsets kept live)
+      const int lim = Nk - key0;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (key0 + acc_row(i, g) >= Nk) s[i] = -__builtin_inff();
+        if (g4 >= lim - acc_row(i, 0)) s[i] = -__builtin_inff();
     }
     float mx = s[0];
 #pragma unroll
@@ -215,7 +226,9 @@ __global__ __launch_bounds__(256, 2) void fwd4_kernel(FwdArgs a) {
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
     if (up) m = mc;
-    const float neg_ref = mine ? -m : -__builtin_inff();  // rows that did not select: p = 0
+    return mine ? -m : -__builtin_inff();
+  };
+  auto softmax_tail = [&](const f32x16& s, float neg_ref, bf16x8 (&pb)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       pb[i >> 3][i & 7] = (__bf16)fast_exp2(__builtin_fmaf(s[i], sl2, neg_ref));
@@ -232,6 +245,39 @@ __global__ __launch_bounds__(256, 2) void fwd4_kernel(FwdArgs a) {
       rs1 = __builtin_amdgcn_fdot2_f32_bf16(p1, one2, rs1, false);
     }
     l += rs0 + rs1;
+  };
+
+  // ---- the softmax tail of one unit interleaved with the S products of the
+  // next: product k, then the probabilities of elements 2k and 2k+1 (scale,
+  // exponential, bf16 pair, pair row sum), fenced so that the compiler keeps
+  // the order; K operand reads run four products ahead.
+  auto tail_and_s = [&](const f32x16& s_in, float neg_ref, bf16x8 (&pb)[2], int st) __attribute__((always_inline)) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+    auto kaddr = [&](int ks) __attribute__((always_inline)) {
+      return reinterpret_cast<const u32x4*>(&lds_k[st][r32 * kHeadDim + (kslot(r32, ks * 2 + g) << 3)]);
+    };
+    u32x4 kf[8];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kf[ks] = *kaddr(ks);
+    f32x16 s = {};
+    float rs[2] = {0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k < 4) kf[k + 4] = *kaddr(k + 4);
+      s = mfma32(as_bf16x8(kf[k]), qf.k[k], s);
+      __builtin_amdgcn_sched_barrier(0);
+      const float e0 = fast_exp2(__builtin_fmaf(s_in[2 * k], sl2, neg_ref));
+      const float e1 = fast_exp2(__builtin_fmaf(s_in[2 * k + 1], sl2, neg_ref));
+      const __bf16 b0 = (__bf16)e0, b1 = (__bf16)e1;
+      pb[k >> 2][(2 * k) & 7] = b0;
+      pb[k >> 2][(2 * k + 1) & 7] = b1;
+      const bf16x2 pr = {b0, b1};
+      rs[k >> 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rs[k >> 2], false);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l += rs[0] + rs[1];
+    return s;
   };
 
   // ---- O^T += V^T P^T: the V^T operand of k-step h2 holds keys
@@ -254,17 +300,18 @@ __global__ __launch_bounds__(256, 2) void fwd4_kernel(FwdArgs a) {
     }
   };
 
-  // ---- unit queue.  After the shift of iteration i, slot j holds unit
-  // i - kAhead + j: slot 0 gets its softmax and PV, slot 1 its S, slot kAhead
-  // was just issued.  Validity / need are wave-uniform bit masks, "mine" (this
-  // row selected the unit's block) a per-lane bit mask; bit j = slot j.
+  // ---- unit queue.  Before the shift of iteration i, slot j holds unit
+  // i - 1 - kAhead + j and sits in stage (st_issue + j) mod kRing: slot 1 gets
+  // its softmax and PV in this iteration (its S tile was computed one
+  // iteration earlier), slot 2 its S; the unit issued now enters slot kAhead.
+  // Validity / need are wave-uniform bit masks, "mine" (this row selected the
+  // unit's block) a per-lane bit mask; bit j = slot j.
   int qkey[kAhead + 1];
 #pragma unroll
   for (int i = 0; i <= kAhead; ++i) qkey[i] = 0;
   uint32_t qneed = 0, qval = 0, qmine = 0;
   int st_issue = 0;
   bool stream_done = false;
-  f32x16 s_cur = {};  // S tile of the unit in slot 1 (before the shift), computed one iteration earlier
 
   // unit sources
   int u_next = t_begin * (KB / kU);                                  // dense
@@ -277,119 +324,139 @@ __global__ __launch_bounds__(256, 2) void fwd4_kernel(FwdArgs a) {
   const u16* klo = SPARSE ? a.klo + (int64_t)h * a.nb_pad * kHeadDim : nullptr;
   const u16* vsum = SPARSE ? a.vsumT + (int64_t)h * kHeadDim * a.nb_pad : nullptr;
 
-  while (true) {
-    // -- softmax of the unit whose PV runs in this iteration (slot 1 before the
-    // shift below); done first so that only its bf16 probabilities, not its S
-    // tile, stay live through routing --
+  // One iteration.  s_in holds the S tile of slot 1, s_out receives that of
+  // slot 2; the loop below alternates the two tiles so that neither is copied.
+  // Returns false once the stream is exhausted and every unit is through its PV.
+  auto iteration = [&](f32x16& s_in, f32x16& s_out) __attribute__((always_inline)) -> bool {
+    const int st1 = st_issue == kRing - 1 ? 0 : st_issue + 1;
+    const int st2 = st1 == kRing - 1 ? 0 : st1 + 1;
+    const bool pv = (qneed & 2u) != 0, do_s = (qneed & 4u) != 0;
     bf16x8 pb[2];
-    const bool pv = (qneed & 2u) != 0;
-    if (pv) softmax(s_cur, qkey[1], (qmine & 2u) != 0, pb);
-    // The tile is dead until the S product below overwrites it; saying so
-    // keeps its registers free through routing.
-    s_cur = __builtin_nondeterministic_value(s_cur);
-
-    // -- next unit of the stream --
-    bool have = false;
-    int key0 = 0;
-    bool mi = false, ne = false;
-    if (!stream_done) {
-      if constexpr (SPARSE) {
-        if (pend_left == 0) {
-          // Route chunks of 32 blocks until one has a selected block: proxy
-          // scores, selection, and the Taylor part of the rejected blocks (at
-          // the current reference m).  Any row of the workgroup selecting a
-          // block makes the block a unit source; `fullA` = this row's
-          // selections, `wvA` = this wave's.
-          while (UA == 0 && c_next < t_end) {
-            const int c0 = c_next;
-            const f32x16 p = proxy_chunk_hl(qf, khi, klo, c0, lane);
-            const float f = fast_exp2(mu * kLog2e - m);  // e^{mu} relative to the reference
-            uint32_t sel_bits = 0;
-            // Weights enter the MFMA as bf16 hi + lo parts: when many blocks
-            // share nearly the same weight, a single bf16 rounding would bias
-            // the Taylor mass coherently instead of averaging out.
-            bf16x8 whi[2], wlo[2];
-            float wden = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int off = acc_row(i, g);
-              const int blk = c0 + off;
-              const bool inr = qvalid && blk < t_end;
-              const bool sel = inr && is_selected(p[i], tau);
-              sel_bits |= (uint32_t)sel << off;
-              const float wt = (inr && !sel) ? (1.f + p[i] - mu) * f : 0.f;
-              __bf16 wh, wl;
-              split_bf16(wt, wh, wl);
-              whi[i >> 3][i & 7] = wh;
-              wlo[i >> 3][i & 7] = wl;
-              const int nj = inr ? min(KB, Nk - blk * KB) : 0;
-              wden = __builtin_fmaf((float)nj, wt, wden);
-            }
-            // Taylor part: O^T += (block sums of V)^T W^T over the chunk, on MFMA
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-              for (int dt = 0; dt < 4; ++dt) {
-                const u32x4 va =
-                    gload<u32x4>(vsum + (int64_t)(dt * 32 + r32) * a.nb_pad + c0 + h2 * 16 + g * 8);
-                o[dt] = mfma32(as_bf16x8(va), whi[h2], o[dt]);
-                o[dt] = mfma32(as_bf16x8(va), wlo[h2], o[dt]);
-              }
-            }
-            l += wden;
-            fullA = sel_bits | partner_b(sel_bits, g);
-            uint32_t w = fullA;
-#pragma unroll
-            for (int sh = 1; sh < 32; sh <<= 1) w |= __shfl_xor(w, sh);
-            w = __builtin_amdgcn_readfirstlane(w);  // equal in all lanes: make it scalar
-            wvA = w;
-            // Exchange the wave masks through the last bytes of the K tile of
-            // the stage about to be refilled: nothing reads that stage until
-            // the unit issued next lands, and the second barrier keeps every
-            // read of the masks ahead of that refill.
-            uint32_t* wmask = reinterpret_cast<uint32_t*>(&lds_k[st_issue][kUE - 8]);
-            if (lane == 0) wmask[wave] = w;
-            __builtin_amdgcn_s_waitcnt(kLgkm0);
-            wg_barrier();
-            uint32_t un = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) un |= wmask[i];
-            UA = __builtin_amdgcn_readfirstlane(un);
-            __builtin_amdgcn_s_waitcnt(kLgkm0);
-            wg_barrier();
-            cA = c0;
-            c_next += kChunk;
-          }
-          if (UA) {
-            const int b = __builtin_ctz(UA);
-            UA &= UA - 1;
-            pend_key = (cA + b) * KB;
-            // units of the block that hold at least one key (the last block
-            // may be ragged)
-            pend_left = min(KB / kU, (Nk - pend_key + kU - 1) / kU);
-            pend_mine = ((fullA >> b) & 1u) != 0;
-            pend_need = ((wvA >> b) & 1u) != 0;
-          }
-        }
-        if (pend_left > 0) {
-          have = true;
-          key0 = pend_key;
-          mi = pend_mine;
-          ne = pend_need;
-          pend_key += kU;
-          --pend_left;
-        }
-      } else {
-        if (u_next < u_end) {
-          have = true;
-          key0 = u_next * kU;
-          mi = ne = true;
-          ++u_next;
-        }
-      }
-      stream_done = !have;
+    float neg_ref = 0.f;
+    if (pv) neg_ref = softmax_head(s_in, qkey[1], (qmine & 2u) != 0);
+    if (pv && do_s) {
+      // The probabilities of slot 1 and the S products of slot 2 do not
+      // depend on each other: interleave about six vector instructions after
+      // each product so that they issue while it runs.
+      s_out = tail_and_s(s_in, neg_ref, pb, st2);
+    } else if (pv) {
+      softmax_tail(s_in, neg_ref, pb);
+      asm volatile("" : "=v"(s_out));  // unused: defined without an instruction
+    } else if (do_s) {
+      u32x4 kf[8];
+      read_k(st2, kf);
+      s_out = mfma_s(kf);
+    } else {
+      asm volatile("" : "=v"(s_out));  // unused: defined without an instruction
     }
+    if (pv) mma_pv(st1, pb);
+
+      // -- next unit of the stream --
+      bool have = false;
+      int key0 = 0;
+      bool mi = false, ne = false;
+      if (!stream_done) {
+        if constexpr (SPARSE) {
+          if (pend_left == 0) {
+            // Route chunks of 32 blocks until one has a selected block: proxy
+            // scores, selection, and the Taylor part of the rejected blocks (at
+            // the current reference m).  Any row of the workgroup selecting a
+            // block makes the block a unit source; `fullA` = this row's
+            // selections, `wvA` = this wave's.
+            while (UA == 0 && c_next < t_end) {
+              const int c0 = c_next;
+              const f32x16 p = proxy_chunk_hl(qf, khi, klo, c0, lane);
+              const float f = fast_exp2(mu * kLog2e - m);  // e^{mu} relative to the reference
+              uint32_t sel_bits = 0;
+              // Weights enter the MFMA as bf16 hi + lo parts: when many blocks
+              // share nearly the same weight, a single bf16 rounding would bias
+              // the Taylor mass coherently instead of averaging out.
+              bf16x8 whi[2], wlo[2];
+              float wden = 0.f;
+              // element i is block c0 + acc_row(i, 0) + 4g: limits are scalar,
+              // the lane term enters through g4 and one shift at the end
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int ci = acc_row(i, 0);
+                const bool inr = qvalid && g4 < t_end - c0 - ci;
+                const bool sel = inr && is_selected(p[i], tau);
+                sel_bits |= (uint32_t)sel << ci;
+                const float wt = (inr && !sel) ? (1.f + p[i] - mu) * f : 0.f;
+                __bf16 wh, wl;
+                split_bf16(wt, wh, wl);
+                whi[i >> 3][i & 7] = wh;
+                wlo[i >> 3][i & 7] = wl;
+                // valid keys of the block (wt = 0 outside the range)
+                const int nj = max(0, min(KB, Nk - (c0 + ci) * KB - g4 * KB));
+                wden = __builtin_fmaf((float)nj, wt, wden);
+              }
+              sel_bits <<= g4;
+              // Taylor part: O^T += (block sums of V)^T W^T over the chunk, on MFMA
+              __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                  const u32x4 va =
+                      gload<u32x4>(vsum + (int64_t)(dt * 32 + r32) * a.nb_pad + c0 + h2 * 16 + g * 8);
+                  o[dt] = mfma32(as_bf16x8(va), whi[h2], o[dt]);
+                  o[dt] = mfma32(as_bf16x8(va), wlo[h2], o[dt]);
+                }
+              }
+              l += wden;
+              fullA = sel_bits | partner_b(sel_bits, g);
+              uint32_t w = fullA;
+#pragma unroll
+              for (int sh = 1; sh < 32; sh <<= 1) w |= __shfl_xor(w, sh);
+              w = __builtin_amdgcn_readfirstlane(w);  // equal in all lanes: make it scalar
+              wvA = w;
+              // Exchange the wave masks through the last bytes of the K tile of
+              // the stage about to be refilled: nothing reads that stage until
+              // the unit issued next lands, and the second barrier keeps every
+              // read of the masks ahead of that refill.
+              uint32_t* wmask = reinterpret_cast<uint32_t*>(&lds_k[st_issue][kUE - 8]);
+              if (lane == 0) wmask[wave] = w;
+              __builtin_amdgcn_s_waitcnt(kLgkm0);
+              wg_barrier();
+              uint32_t un = 0;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) un |= wmask[i];
+              UA = __builtin_amdgcn_readfirstlane(un);
+              __builtin_amdgcn_s_waitcnt(kLgkm0);
+              wg_barrier();
+              cA = c0;
+              c_next += kChunk;
+            }
+            if (UA) {
+              const int b = __builtin_ctz(UA);
+              UA &= UA - 1;
+              pend_key = (cA + b) * KB;
+              // units of the block that hold at least one key (the last block
+              // may be ragged)
+              pend_left = min(KB / kU, (Nk - pend_key + kU - 1) / kU);
+              pend_mine = ((fullA >> b) & 1u) != 0;
+              pend_need = ((wvA >> b) & 1u) != 0;
+            }
+          }
+          if (pend_left > 0) {
+            have = true;
+            key0 = pend_key;
+            mi = pend_mine;
+            ne = pend_need;
+            pend_key += kU;
+            --pend_left;
+          }
+        } else {
+          if (u_next < u_end) {
+            have = true;
+            key0 = u_next * kU;
+            mi = ne = true;
+            ++u_next;
+          }
+        }
+        stream_done = !have;
+      }
+
     // -- issue the newest unit (a stream past its end reloads key 0 into a
     // stage nobody reads, so the count of loads in flight stays exact) --
     dma_unit(key0, st_issue);
@@ -399,20 +466,14 @@ __global__ __launch_bounds__(256, 2) void fwd4_kernel(FwdArgs a) {
     qval = (qval >> 1) | ((uint32_t)have << kAhead);
     qneed = (qneed >> 1) | ((uint32_t)(have && ne) << kAhead);
     qmine = (qmine >> 1) | ((uint32_t)(have && mi) << kAhead);
-    // slot j sits in stage (st_issue + 1 + j) mod kRing
-    const int st0 = st_issue == kRing - 1 ? 0 : st_issue + 1;
-    const int st1 = st0 == kRing - 1 ? 0 : st0 + 1;
-
-    if (qneed & 2u)
-      s_cur = mma_s(st1);
-    else
-      asm volatile("" : "=v"(s_cur));  // unused: defined without an instruction
-    if (pv) mma_pv(st0, pb);
-    st_issue = st0;  // slot 0's stage is refilled next, after the barrier
-    __builtin_amdgcn_s_waitcnt(kWaitNext);  // this wave's loads of slots 1 and 2 landed
+    st_issue = st1;  // slot 1's stage (slot 0 after the shift) is refilled next
+    __builtin_amdgcn_s_waitcnt(kWaitNext);  // this wave's loads of the next two units landed
     wg_barrier();                           // ... and every wave's
     // done when the stream is exhausted and no issued unit awaits its PV
-    if (stream_done && (qval >> 1) == 0) break;
+    return !(stream_done && (qval >> 1) == 0);
+  };
+  f32x16 sA = {}, sB = {};
+  while (iteration(sA, sB) && iteration(sB, sA)) {
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
 
