@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBS = 8000.0
 METRIC = "ms/call + dense-equivalent TFLOP/s (% bf16 MFMA peak), 4K Stage-2 sparse attention"
-KERNEL_SOURCES = ["block_sparse_attention_06_amd/csrc/forward4.hip",
+KERNEL_SOURCES = ["block_sparse_attention_06_amd/csrc/forward.hip",
                   "block_sparse_attention_06_amd/csrc/device.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_sparse_4k_beta0.5_traffic.json")
 

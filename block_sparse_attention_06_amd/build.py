@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsolattn.so")
-SOURCES = ["api.hip", "pool_stats.hip", "forward.hip", "forward_pp.hip", "forward4.hip"]
+SOURCES = ["api.hip", "pool_stats.hip", "forward.hip", "forward_pp.hip", "merge.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -19,6 +19,7 @@ FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-shared",
+    "-fvisibility=hidden",  # only the C ABI declared in include/solattn.h is exported
     # no packed-fp32 instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",

@@ -182,19 +182,17 @@ int sol_attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, ui
     f.part_o = (float*)(ws + p.off_po);
     f.part_ml = (float*)(ws + p.off_pml);
   }
-  // Sparse attention runs the pipelined 4-wave kernel; dense attention over
-  // long sequences (no key split) the 8-wave ping-pong kernel on 256-row
-  // tiles; dense short query sets and split keys the 4-wave kernel.
+  // Dense attention over long sequences (no key split) runs the 8-wave
+  // ping-pong kernel on 256-row tiles; sparse attention, dense short query
+  // sets and split keys the pipelined 4-wave kernel.
   const long long pp_wgs = (long long)H * cdiv(N, 256);
   const bool use_pp = !sparse && f.splits == 1 && pp_wgs >= kCUs;
-  if (sparse) {
-    if (int r = hip_status(launch_forward4(f, true, B, s))) return r;
-  } else if (use_pp) {
+  if (use_pp) {
     FwdArgs fp = f;
     fp.total = (int)pp_wgs;
     if (int r = hip_status(launch_forward_pp(fp, false, 128, s))) return r;
   } else {
-    if (int r = hip_status(launch_forward(f, false, 128, s))) return r;
+    if (int r = hip_status(launch_forward(f, sparse, sparse ? B : 128, s))) return r;
   }
   if (f.splits > 1) {
     CombineArgs c{f.part_o, f.part_ml, out, lse, N, H, f.splits};

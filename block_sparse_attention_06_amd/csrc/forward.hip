@@ -1,6 +1,6 @@
-// Fused attention forward for gfx950: dense softmax attention, and
-// query-thresholded block-sparse attention with a first-order Taylor term for
-// the rejected blocks, in one online-softmax pass.
+// Fused attention forward for gfx950 with a pipelined key loop: dense softmax
+// attention, and query-thresholded block-sparse attention with a first-order
+// Taylor term for the rejected blocks, in one online-softmax pass.
 //
 // Sol-Engine LTX25 page, "Stage 2 Optimization -- Core Technology: Sol-Attn":
 //  - routing is folded into the softmax pass: pooled keys are taken 32 blocks
@@ -15,15 +15,18 @@
 //
 // Workgroup: 4 waves x 32 query rows = 128 rows of one head; two workgroups
 // per CU.  Keys stream through LDS in units of 32 rows of K and V, in a ring of
-// five stages filled by direct global->LDS loads four units ahead of the unit
-// being computed (no registers hold data in flight; each wave waits only for
-// its own loads of the next unit, then one barrier per unit publishes it).
-// Rows sit row-major with XOR-swizzled 16-byte chunks.  Each wave computes
-// S^T = K Q^T and O^T += V^T P^T on bf16 MFMA (fp32 accumulation); the V^T
-// operand comes straight from the row-major tile through the transposing LDS
-// read.  A unit is fetched when any wave of the workgroup selected its block;
-// a wave issues MFMAs only when one of its own 32 rows did, and rows that did
-// not select it get zero probability.
+// five stages filled by direct global->LDS loads.  A load takes a scalar base
+// (the unit's first key) and a per-lane offset fixed for the whole kernel, so
+// issuing a unit costs no vector arithmetic.
+//
+// Per iteration each wave (1) runs the online softmax of the oldest unit in
+// flight on its S tile, computed one iteration earlier, (2) routes and issues
+// the loads of the newest unit, (3) issues the S^T = K Q^T products of the next
+// unit, and (4) issues O^T += V^T P^T for the oldest unit.  The softmax therefore never
+// waits for its own products, and the matrix products of (3) and (4) run while
+// the wave crosses the barrier and starts the next softmax.  Each wave then
+// waits only for its own loads of the unit whose S comes next, and one barrier
+// per unit publishes them and frees the stage refilled next.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -31,68 +34,78 @@ namespace solattn {
 
 namespace {
 
-constexpr int kUnit = 32;                        // keys per staged unit
-constexpr int kStageElems = kUnit * kHeadDim;    // bf16 per tensor per stage
-constexpr float kRescaleSlack = 8.f;             // log2 units the reference may lag the max
+constexpr int kU = 32;                  // keys per staged unit
+constexpr int kUE = kU * kHeadDim;      // bf16 per tensor per stage
+constexpr int kRing = 5;                // LDS stages (80 KiB: two workgroups per CU)
+constexpr int kAhead = kRing - 1;       // units in flight beyond the one whose PV runs
+constexpr int kDmaPerUnit = 4;          // loads per wave per unit: 2 groups of 4 rows, K and V
+constexpr float kSlack = 8.f;           // log2 units the reference may lag the row max
+constexpr int kLgkm0 = 0xC07F;          // s_waitcnt lgkmcnt(0)
+
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(n) alone.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+// At the end of an iteration the loads of the next two units (S next, PV
+// after) must have landed; the kAhead - 2 younger units may still be in flight.
+constexpr int kWaitNext = vmcnt_imm(kDmaPerUnit * (kAhead - 2));
 
 // LDS layouts of a unit ([32 rows][128 bf16], 16-byte chunks): K rows put
 // chunk c at c ^ (row % 16), so the S operand reads 16 consecutive rows at one
 // chunk without bank conflicts; V rows put chunk c at c ^ 4 (row % 4), so the
 // transposing read of 4 consecutive rows x 4 chunks per 16 lanes is
 // conflict-free.
-__device__ __forceinline__ int k_slot(int row, int c) { return c ^ (row & 15); }
-__device__ __forceinline__ int v_slot(int row, int c) { return c ^ ((row & 3) << 2); }
+__device__ __forceinline__ int kslot(int row, int c) { return c ^ (row & 15); }
+__device__ __forceinline__ int vslot(int row, int c) { return c ^ ((row & 3) << 2); }
 
-// LDS ring depth.  Four-wave workgroups run two per CU and share 160 KiB:
-// five 16 KiB stages each (loads four units ahead).  Eight-wave workgroups run
-// one per CU and use eight stages (seven units ahead).
-template <bool SPARSE, int WAVES>
-constexpr int stages() { return WAVES == 8 ? 8 : 5; }
+// Direct global -> LDS load of 16 bytes per lane from sbase + voff (sbase
+// wave-uniform, voff a 32-bit per-lane byte offset); lane l's bytes land at LDS
+// byte address lds + 16 l.  Inline assembly keeps the compiler from treating
+// it as a pending write to all of LDS; the caller orders it with explicit
+// vector-memory waits and barriers.
+__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
 
-// s_waitcnt immediate (gfx9 encoding) for vmcnt(n) alone.
-constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
-
-// Each wave issues 16 / WAVES loads per unit; waiting until only the loads of
-// the stages - 2 later units are in flight means this wave's loads of the next
-// unit have landed.
-template <bool SPARSE, int WAVES>
-constexpr int wait_next_unit() { return vm_wait((16 / WAVES) * (stages<SPARSE, WAVES>() - 2)); }
-constexpr int kWaitLgkm0 = 0xC07F;
-
-__device__ __forceinline__ float partner(float x, int g) {
+__device__ __forceinline__ float partner_f(float x, int g) {
   // value of lane l ^ 32
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(g ? r[0] : r[1]);
 }
 
-__device__ __forceinline__ uint32_t partner_u(uint32_t x, int g) {
+__device__ __forceinline__ uint32_t partner_b(uint32_t x, int g) {
   const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
   return g ? r[0] : r[1];
 }
 
+// Workgroup barrier that is also a compiler barrier for memory accesses (the
+// hardware barrier alone does not stop the compiler from moving LDS reads).
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace
 
-template <bool SPARSE, int KB, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 2) void fwd_kernel(FwdArgs a) {
-  constexpr int kStages = stages<SPARSE, WAVES>();
-  constexpr int kWaitNext = wait_next_unit<SPARSE, WAVES>();
-  constexpr int kRowsPerWave = kUnit / WAVES;  // unit rows each wave loads
-  __shared__ __attribute__((aligned(16))) u16 lds_k[kStages][kStageElems];
-  __shared__ __attribute__((aligned(16))) u16 lds_v[kStages][kStageElems];
+template <bool SPARSE, int KB>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 lds_k[kRing][kUE];
+  __shared__ __attribute__((aligned(16))) u16 lds_v[kRing][kUE];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+  const int g4 = g * 4;  // accumulator element i of lane half g is row acc_row(i, 0) + g4
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // Natural order: consecutive workgroups take consecutive query tiles of one
   // head and are dealt to the 8 XCDs round-robin, so all XCDs work on the same
-  // one or two heads at a time and those heads' keys and values stay in the
-  // memory-side cache.
+  // one or two heads at a time.
   const int logical = blockIdx.x;
   if (logical >= a.total) return;
   const int split = logical % a.splits;
   const int tq = logical / a.splits;
   const int qt = tq % a.n_qt, h = tq / a.n_qt;
-  const int row = qt * (32 * WAVES) + wave * 32 + r32;
+  const int row = qt * kQTile + wave * 32 + r32;
   const bool qvalid = row < a.N;
 
   QFrag qf;
@@ -109,7 +122,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
   float l = 0.f;  // this lane's share of the denominator, relative to 2^m
-  float m;        // reference of the running sums (log2 units), within kRescaleSlack of the max
+  float m;        // reference of the running sums (log2 units), within kSlack of the max
   float mu = 0.f, tau = __builtin_inff();
   if constexpr (SPARSE) {
     if (qvalid) {
@@ -123,46 +136,89 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_kernel(FwdArgs a) {
 
   // The query fragment and row statistics are the only loads the compiler
   // tracks; drain them here so that no wait it places later also waits for
-  // the key/value prefetches below (which it does not track).
+  // the key/value loads below (which it does not track).
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- direct global -> LDS loads of one unit: wave w fills K and V rows
-  // w*32/WAVES onwards, four rows (1 KiB) per instruction; lane l lands in chunk slot
-  // l % 16 of row l / 16 and fetches the global chunk that slot holds.
-  // Rows past the last key re-read the last key (finite data): their scores
-  // are masked and their probabilities are zero.
-  auto dma_unit = [&](int key0, int st) __attribute__((always_inline)) {
+  // ---- direct loads of one unit: wave w fills K and V rows 8w .. 8w+7 in two
+  // groups of four rows (1 KiB per instruction); lane l lands in chunk slot
+  // l % 16 of row l / 16 of its group and fetches the global chunk that slot
+  // holds.  Offsets are relative to the unit's first key.
+  const int slot = lane & 15;
+  uint32_t offk[2], offv[2];
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave / 4; ++i) {
-      const int r0 = wave * kRowsPerWave + i * 4;
-      const int r = r0 + (lane >> 4), slot = lane & 15;
-      const int64_t key = min(key0 + r, Nk - 1);
-      dma_to_lds16(kh + key * kHeadDim + (k_slot(r, slot) << 3), lds_addr(&lds_k[st][r0 * kHeadDim]));
-      dma_to_lds16(vh + key * kHeadDim + (v_slot(r, slot) << 3), lds_addr(&lds_v[st][r0 * kHeadDim]));
+  for (int i = 0; i < 2; ++i) {
+    const int r = wave * 8 + i * 4 + (lane >> 4);
+    offk[i] = (uint32_t)(r * kHeadDim + (kslot(r, slot) << 3)) * 2u;
+    offv[i] = (uint32_t)(r * kHeadDim + (vslot(r, slot) << 3)) * 2u;
+  }
+  // Every unit of the stream starts at a key < Nk (key 0 for the stream past
+  // its end); the clamp below keeps even a violation of that inside the buffer.
+  auto dma_unit = [&](int key0, int st) __attribute__((always_inline)) {
+    key0 = min(__builtin_amdgcn_readfirstlane(key0), Nk - 1);
+    st = __builtin_amdgcn_readfirstlane(st);
+    const u16* kb = kh + (int64_t)key0 * kHeadDim;
+    const u16* vb = vh + (int64_t)key0 * kHeadDim;
+    if (key0 + kU <= Nk) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r0 = wave * 8 + i * 4;
+        dma16_sv(kb, offk[i], lds_addr(&lds_k[st][r0 * kHeadDim]));
+        dma16_sv(vb, offv[i], lds_addr(&lds_v[st][r0 * kHeadDim]));
+      }
+    } else {
+      // ragged last unit: rows past the last key re-read the last key (finite
+      // data); their scores are masked and their probabilities are zero
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r0 = wave * 8 + i * 4;
+        const int r = r0 + (lane >> 4);
+        const int rr = min(r, Nk - 1 - key0);
+        const uint32_t ok = (uint32_t)(rr * kHeadDim + (kslot(r, slot) << 3)) * 2u;
+        const uint32_t ov = (uint32_t)(rr * kHeadDim + (vslot(r, slot) << 3)) * 2u;
+        dma16_sv(kb, ok, lds_addr(&lds_k[st][r0 * kHeadDim]));
+        dma16_sv(vb, ov, lds_addr(&lds_v[st][r0 * kHeadDim]));
+      }
     }
   };
 
-  // ---- exact online-softmax update with one staged unit ----
-  auto compute = [&](int st, int key0, bool mine) __attribute__((always_inline)) {
+  // ---- S^T = K Q^T of one staged unit (consumed an iteration later): operand
+  // reads and products separately, so the products can be interleaved with
+  // other work.
+  auto read_k = [&](int st, u32x4 (&kf)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      kf[ks] = *reinterpret_cast<const u32x4*>(&lds_k[st][r32 * kHeadDim + (kslot(r32, ks * 2 + g) << 3)]);
+  };
+  auto mfma_s = [&](const u32x4 (&kf)[8]) __attribute__((always_inline)) {
     f32x16 s = {};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(
-          &lds_k[st][r32 * kHeadDim + (k_slot(r32, ks * 2 + g) << 3)]);
-      s = mfma32(as_bf16x8(ka), qf.k[ks], s);
-    }
-    if (key0 + kUnit > Nk) {  // ragged last unit: keys past the end do not exist
+    for (int ks = 0; ks < 8; ++ks) s = mfma32(as_bf16x8(kf[ks]), qf.k[ks], s);
+    return s;
+  };
+
+  // ---- online softmax of one unit's S tile, in two parts.  The head masks
+  // keys past the end, finds the row max and moves the reference (m, with o
+  // and l rescaled) when the max outruns it; it returns the exponent offset
+  // (-m, or -inf for rows that did not select the unit: p = 0).  The tail
+  // forms the probabilities as the bf16 B operand of the PV product (keys
+  // permuted within 16 as the accumulator layout holds them) and adds their
+  // row sums to l.
+  auto softmax_head = [&](f32x16& s, int key0, bool mine) __attribute__((always_inline)) {
+    if (key0 + kU > Nk) {  // ragged last unit: keys past the end do not exist
+      // element i holds key offset acc_row(i, 0) + 4g: compare the one
+      // per-lane term with scalar limits (no per-element lane offsets kept live)
+      const int lim = Nk - key0;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (key0 + acc_row(i, g) >= Nk) s[i] = -__builtin_inff();
+        if (g4 >= lim - acc_row(i, 0)) s[i] = -__builtin_inff();
     }
     float mx = s[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, partner(mx, g));
+    mx = fmaxf(mx, partner_f(mx, g));
     const float mc = mx * sl2;
     // move the reference only when the max outruns it by more than the slack
-    const bool up = mine && (mc > m + kRescaleSlack);
+    const bool up = mine && (mc > m + kSlack);
     if (__ballot(up)) {
       const float alpha = up ? fast_exp2(m - mc) : 1.f;
       l *= alpha;
@@ -170,8 +226,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_kernel(FwdArgs a) {
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
     if (up) m = mc;
-    const float neg_ref = mine ? -m : -__builtin_inff();  // rows that did not select: p = 0
-    bf16x8 pb[2];
+    return mine ? -m : -__builtin_inff();
+  };
+  auto softmax_tail = [&](const f32x16& s, float neg_ref, bf16x8 (&pb)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       pb[i >> 3][i & 7] = (__bf16)fast_exp2(__builtin_fmaf(s[i], sl2, neg_ref));
@@ -179,18 +236,54 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_kernel(FwdArgs a) {
     // per instruction: dot(p_pair, (1, 1)) accumulated in fp32.
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2 p0 = {pb[0][2 * e], pb[0][2 * e + 1]};
+      const bf16x2 p1 = {pb[1][2 * e], pb[1][2 * e + 1]};
+      rs0 = __builtin_amdgcn_fdot2_f32_bf16(p0, one2, rs0, false);
+      rs1 = __builtin_amdgcn_fdot2_f32_bf16(p1, one2, rs1, false);
+    }
+    l += rs0 + rs1;
+  };
+
+  // ---- the softmax tail of one unit interleaved with the S products of the
+  // next: product k, then the probabilities of elements 2k and 2k+1 (scale,
+  // exponential, bf16 pair, pair row sum), fenced so that the compiler keeps
+  // the order; K operand reads run four products ahead.
+  auto tail_and_s = [&](const f32x16& s_in, float neg_ref, bf16x8 (&pb)[2], int st) __attribute__((always_inline)) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+    auto kaddr = [&](int ks) __attribute__((always_inline)) {
+      return reinterpret_cast<const u32x4*>(&lds_k[st][r32 * kHeadDim + (kslot(r32, ks * 2 + g) << 3)]);
+    };
+    u32x4 kf[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16x2 pr = {pb[t][2 * e], pb[t][2 * e + 1]};
-        rsum[e] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rsum[e], false);
-      }
-    l += (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
-    // O^T += V^T P^T: the V^T operand of k-step h2 holds keys
-    // h2*16 + {4g..4g+3, 8+4g..8+4g+3} -- the keys of P this lane half holds --
-    // read as two transposed 4 x 16 blocks per 16-lane group.
+    for (int ks = 0; ks < 4; ++ks) kf[ks] = *kaddr(ks);
+    f32x16 s = {};
+    float rs[2] = {0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k < 4) kf[k + 4] = *kaddr(k + 4);
+      s = mfma32(as_bf16x8(kf[k]), qf.k[k], s);
+      __builtin_amdgcn_sched_barrier(0);
+      const float e0 = fast_exp2(__builtin_fmaf(s_in[2 * k], sl2, neg_ref));
+      const float e1 = fast_exp2(__builtin_fmaf(s_in[2 * k + 1], sl2, neg_ref));
+      const __bf16 b0 = (__bf16)e0, b1 = (__bf16)e1;
+      pb[k >> 2][(2 * k) & 7] = b0;
+      pb[k >> 2][(2 * k + 1) & 7] = b1;
+      const bf16x2 pr = {b0, b1};
+      rs[k >> 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rs[k >> 2], false);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l += rs[0] + rs[1];
+    return s;
+  };
+
+  // ---- O^T += V^T P^T: the V^T operand of k-step h2 holds keys
+  // h2*16 + {4g..4g+3, 8+4g..8+4g+3} -- the keys of P this lane half holds --
+  // read as two transposed 4 x 16 blocks per 16-lane group.
+  auto mma_pv = [&](int st, const bf16x8 (&pb)[2]) __attribute__((always_inline)) {
     const int G = lane >> 4, j = lane & 15;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -198,34 +291,32 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const int col = dt * 32 + (G & 1) * 16 + 4 * (j & 3);
-        const u32x2 v0 = lds_read_tr16(&lds_v[st][r0 * kHeadDim + (v_slot(r0, col >> 3) << 3) + (col & 7)]);
-        const u32x2 v1 = lds_read_tr16(&lds_v[st][(r0 + 8) * kHeadDim + (v_slot(r0 + 8, col >> 3) << 3) + (col & 7)]);
+        const u32x2 v0 = lds_read_tr16(&lds_v[st][r0 * kHeadDim + (vslot(r0, col >> 3) << 3) + (col & 7)]);
+        const u32x2 v1 =
+            lds_read_tr16(&lds_v[st][(r0 + 8) * kHeadDim + (vslot(r0 + 8, col >> 3) << 3) + (col & 7)]);
         const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
         o[dt] = mfma32(as_bf16x8(va), pb[h2], o[dt]);
       }
     }
   };
 
-  // ---- one loop: iteration t issues the loads of unit t into stage t % S and
-  // computes unit t - A (A = S - 1), issued A iterations earlier.  Unit slots
-  // shift by one per iteration, so every index is static.  Once the stream is
-  // exhausted, iterations load key 0 into a stage nobody reads (keeping the
-  // count of loads in flight exact) until the last unit is computed.
-  constexpr int A = kStages - 1;
-  int qkey[A + 1];
-  bool qmine[A + 1], qneed[A + 1], qval[A + 1];
+  // ---- unit queue.  Before the shift of iteration i, slot j holds unit
+  // i - 1 - kAhead + j and sits in stage (st_issue + j) mod kRing: slot 1 gets
+  // its softmax and PV in this iteration (its S tile was computed one
+  // iteration earlier), slot 2 its S; the unit issued now enters slot kAhead.
+  // Validity / need are wave-uniform bit masks, "mine" (this row selected the
+  // unit's block) a per-lane bit mask; bit j = slot j.
+  int qkey[kAhead + 1];
 #pragma unroll
-  for (int i = 0; i <= A; ++i) {
-    qkey[i] = 0;
-    qmine[i] = qneed[i] = qval[i] = false;
-  }
+  for (int i = 0; i <= kAhead; ++i) qkey[i] = 0;
+  uint32_t qneed = 0, qval = 0, qmine = 0;
   int st_issue = 0;
   bool stream_done = false;
 
   // unit sources
-  int u_next = t_begin * (KB / kUnit);                                 // dense
-  const int u_end = min(t_end * (KB / kUnit), (Nk + kUnit - 1) / kUnit);
-  int c_next = t_begin, cA = 0;                                        // sparse
+  int u_next = t_begin * (KB / kU);                                  // dense
+  const int u_end = min(t_end * (KB / kU), (Nk + kU - 1) / kU);
+  int c_next = t_begin, cA = 0;                                      // sparse
   uint32_t UA = 0, fullA = 0, wvA = 0;
   int pend_left = 0, pend_key = 0;
   bool pend_mine = false, pend_need = false;
@@ -233,134 +324,161 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_kernel(FwdArgs a) {
   const u16* klo = SPARSE ? a.klo + (int64_t)h * a.nb_pad * kHeadDim : nullptr;
   const u16* vsum = SPARSE ? a.vsumT + (int64_t)h * kHeadDim * a.nb_pad : nullptr;
 
-  while (true) {
-    // -- next unit of the stream --
-    bool have = false;
-    int key0 = 0;
-    bool mi = false, ne = false;
-    if (!stream_done) {
-      if constexpr (SPARSE) {
-        if (pend_left == 0) {
-          // Route chunks of 32 blocks until one has a selected block: proxy
-          // scores, selection, and the Taylor part of the rejected blocks (at
-          // the current reference m).  Any row of the workgroup selecting a
-          // block makes the block a unit source; `fullA` = this row's
-          // selections, `wvA` = this wave's.
-          while (UA == 0 && c_next < t_end) {
-            const int c0 = c_next;
-            const f32x16 p = proxy_chunk_hl(qf, khi, klo, c0, lane);
-            const float f = fast_exp2(mu * kLog2e - m);  // e^{mu} relative to the reference
-            uint32_t sel_bits = 0;
-            // Weights enter the MFMA as bf16 hi + lo parts: when many blocks
-            // share nearly the same weight, a single bf16 rounding would bias
-            // the Taylor mass coherently instead of averaging out.
-            bf16x8 whi[2], wlo[2];
-            float wden = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int off = acc_row(i, g);
-              const int blk = c0 + off;
-              const bool inr = qvalid && blk < t_end;
-              const bool sel = inr && is_selected(p[i], tau);
-              sel_bits |= (uint32_t)sel << off;
-              const float wt = (inr && !sel) ? (1.f + p[i] - mu) * f : 0.f;
-              __bf16 wh, wl;
-              split_bf16(wt, wh, wl);
-              whi[i >> 3][i & 7] = wh;
-              wlo[i >> 3][i & 7] = wl;
-              const int nj = inr ? min(KB, Nk - blk * KB) : 0;
-              wden = __builtin_fmaf((float)nj, wt, wden);
-            }
-            // Taylor part: O^T += (block sums of V)^T W^T over the chunk, on MFMA
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-              for (int dt = 0; dt < 4; ++dt) {
-                const u32x4 va =
-                    gload<u32x4>(vsum + (int64_t)(dt * 32 + r32) * a.nb_pad + c0 + h2 * 16 + g * 8);
-                o[dt] = mfma32(as_bf16x8(va), whi[h2], o[dt]);
-                o[dt] = mfma32(as_bf16x8(va), wlo[h2], o[dt]);
-              }
-            }
-            l += wden;
-            fullA = sel_bits | partner_u(sel_bits, g);
-            uint32_t w = fullA;
-#pragma unroll
-            for (int sh = 1; sh < 32; sh <<= 1) w |= __shfl_xor(w, sh);
-            wvA = w;
-            // Exchange the wave masks through the last bytes of the K tile of
-            // the stage about to be refilled: nothing reads it until the unit
-            // issued next lands, and the second barrier keeps every read of the
-            // masks ahead of that refill.
-            uint32_t* wmask = reinterpret_cast<uint32_t*>(&lds_k[st_issue][kStageElems - 2 * WAVES]);
-            if (lane == 0) wmask[wave] = w;
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-            __builtin_amdgcn_s_barrier();
-            uint32_t un = 0;
-#pragma unroll
-            for (int i = 0; i < WAVES; ++i) un |= wmask[i];
-            UA = un;
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-            __builtin_amdgcn_s_barrier();
-            cA = c0;
-            c_next += kChunk;
-          }
-          if (UA) {
-            const int b = __builtin_ctz(UA);
-            UA &= UA - 1;
-            pend_key = (cA + b) * KB;
-            pend_left = KB / kUnit;
-            pend_mine = ((fullA >> b) & 1u) != 0;
-            pend_need = ((wvA >> b) & 1u) != 0;
-          }
-        }
-        if (pend_left > 0) {
-          have = true;
-          key0 = pend_key;
-          mi = pend_mine;
-          ne = pend_need;
-          pend_key += kUnit;
-          --pend_left;
-        }
-      } else {
-        if (u_next < u_end) {
-          have = true;
-          key0 = u_next * kUnit;
-          mi = ne = true;
-          ++u_next;
-        }
-      }
-      stream_done = !have;
+  // One iteration.  s_in holds the S tile of slot 1, s_out receives that of
+  // slot 2; the loop below alternates the two tiles so that neither is copied.
+  // Returns false once the stream is exhausted and every unit is through its PV.
+  auto iteration = [&](f32x16& s_in, f32x16& s_out) __attribute__((always_inline)) -> bool {
+    const int st1 = st_issue == kRing - 1 ? 0 : st_issue + 1;
+    const int st2 = st1 == kRing - 1 ? 0 : st1 + 1;
+    const bool pv = (qneed & 2u) != 0, do_s = (qneed & 4u) != 0;
+    bf16x8 pb[2];
+    float neg_ref = 0.f;
+    if (pv) neg_ref = softmax_head(s_in, qkey[1], (qmine & 2u) != 0);
+    if (pv && do_s) {
+      // The probabilities of slot 1 and the S products of slot 2 do not
+      // depend on each other: interleave about six vector instructions after
+      // each product so that they issue while it runs.
+      s_out = tail_and_s(s_in, neg_ref, pb, st2);
+    } else if (pv) {
+      softmax_tail(s_in, neg_ref, pb);
+      asm volatile("" : "=v"(s_out));  // unused: defined without an instruction
+    } else if (do_s) {
+      u32x4 kf[8];
+      read_k(st2, kf);
+      s_out = mfma_s(kf);
+    } else {
+      asm volatile("" : "=v"(s_out));  // unused: defined without an instruction
     }
-    bool pending = false;  // units issued but not yet computed
-#pragma unroll
-    for (int i = 1; i <= A; ++i) pending |= qval[i];
-    if (stream_done && !pending) break;
+    if (pv) mma_pv(st1, pb);
 
-    // -- issue unit t, shift the slots, compute unit t - A --
+      // -- next unit of the stream --
+      bool have = false;
+      int key0 = 0;
+      bool mi = false, ne = false;
+      if (!stream_done) {
+        if constexpr (SPARSE) {
+          if (pend_left == 0) {
+            // Route chunks of 32 blocks until one has a selected block: proxy
+            // scores, selection, and the Taylor part of the rejected blocks (at
+            // the current reference m).  Any row of the workgroup selecting a
+            // block makes the block a unit source; `fullA` = this row's
+            // selections, `wvA` = this wave's.
+            while (UA == 0 && c_next < t_end) {
+              const int c0 = c_next;
+              const f32x16 p = proxy_chunk_hl(qf, khi, klo, c0, lane);
+              const float f = fast_exp2(mu * kLog2e - m);  // e^{mu} relative to the reference
+              uint32_t sel_bits = 0;
+              // Weights enter the MFMA as bf16 hi + lo parts: when many blocks
+              // share nearly the same weight, a single bf16 rounding would bias
+              // the Taylor mass coherently instead of averaging out.
+              bf16x8 whi[2], wlo[2];
+              float wden = 0.f;
+              // element i is block c0 + acc_row(i, 0) + 4g: limits are scalar,
+              // the lane term enters through g4 and one shift at the end
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int ci = acc_row(i, 0);
+                const bool inr = qvalid && g4 < t_end - c0 - ci;
+                const bool sel = inr && is_selected(p[i], tau);
+                sel_bits |= (uint32_t)sel << ci;
+                const float wt = (inr && !sel) ? (1.f + p[i] - mu) * f : 0.f;
+                __bf16 wh, wl;
+                split_bf16(wt, wh, wl);
+                whi[i >> 3][i & 7] = wh;
+                wlo[i >> 3][i & 7] = wl;
+                // valid keys of the block (wt = 0 outside the range)
+                const int nj = max(0, min(KB, Nk - (c0 + ci) * KB - g4 * KB));
+                wden = __builtin_fmaf((float)nj, wt, wden);
+              }
+              sel_bits <<= g4;
+              // Taylor part: O^T += (block sums of V)^T W^T over the chunk, on MFMA
+              __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                  const u32x4 va =
+                      gload<u32x4>(vsum + (int64_t)(dt * 32 + r32) * a.nb_pad + c0 + h2 * 16 + g * 8);
+                  o[dt] = mfma32(as_bf16x8(va), whi[h2], o[dt]);
+                  o[dt] = mfma32(as_bf16x8(va), wlo[h2], o[dt]);
+                }
+              }
+              l += wden;
+              fullA = sel_bits | partner_b(sel_bits, g);
+              uint32_t w = fullA;
+#pragma unroll
+              for (int sh = 1; sh < 32; sh <<= 1) w |= __shfl_xor(w, sh);
+              w = __builtin_amdgcn_readfirstlane(w);  // equal in all lanes: make it scalar
+              wvA = w;
+              // Exchange the wave masks through the last bytes of the K tile of
+              // the stage about to be refilled: nothing reads that stage until
+              // the unit issued next lands, and the second barrier keeps every
+              // read of the masks ahead of that refill.
+              uint32_t* wmask = reinterpret_cast<uint32_t*>(&lds_k[st_issue][kUE - 8]);
+              if (lane == 0) wmask[wave] = w;
+              __builtin_amdgcn_s_waitcnt(kLgkm0);
+              wg_barrier();
+              uint32_t un = 0;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) un |= wmask[i];
+              UA = __builtin_amdgcn_readfirstlane(un);
+              __builtin_amdgcn_s_waitcnt(kLgkm0);
+              wg_barrier();
+              cA = c0;
+              c_next += kChunk;
+            }
+            if (UA) {
+              const int b = __builtin_ctz(UA);
+              UA &= UA - 1;
+              pend_key = (cA + b) * KB;
+              // units of the block that hold at least one key (the last block
+              // may be ragged)
+              pend_left = min(KB / kU, (Nk - pend_key + kU - 1) / kU);
+              pend_mine = ((fullA >> b) & 1u) != 0;
+              pend_need = ((wvA >> b) & 1u) != 0;
+            }
+          }
+          if (pend_left > 0) {
+            have = true;
+            key0 = pend_key;
+            mi = pend_mine;
+            ne = pend_need;
+            pend_key += kU;
+            --pend_left;
+          }
+        } else {
+          if (u_next < u_end) {
+            have = true;
+            key0 = u_next * kU;
+            mi = ne = true;
+            ++u_next;
+          }
+        }
+        stream_done = !have;
+      }
+
+    // -- issue the newest unit (a stream past its end reloads key 0 into a
+    // stage nobody reads, so the count of loads in flight stays exact) --
     dma_unit(key0, st_issue);
 #pragma unroll
-    for (int i = 0; i < A; ++i) {
-      qkey[i] = qkey[i + 1];
-      qmine[i] = qmine[i + 1];
-      qneed[i] = qneed[i + 1];
-      qval[i] = qval[i + 1];
-    }
-    qkey[A] = key0;
-    qmine[A] = mi;
-    qneed[A] = ne;
-    qval[A] = have;
-    const int st_comp = st_issue == kStages - 1 ? 0 : st_issue + 1;
-    st_issue = st_comp;
-    if (qval[0] && qneed[0]) compute(st_comp, qkey[0], qmine[0]);
-    __builtin_amdgcn_s_waitcnt(kWaitNext);  // this wave's loads of the next unit landed
-    __builtin_amdgcn_s_barrier();           // ... and every wave's; its stage is free to refill
+    for (int i = 0; i < kAhead; ++i) qkey[i] = qkey[i + 1];
+    qkey[kAhead] = key0;
+    qval = (qval >> 1) | ((uint32_t)have << kAhead);
+    qneed = (qneed >> 1) | ((uint32_t)(have && ne) << kAhead);
+    qmine = (qmine >> 1) | ((uint32_t)(have && mi) << kAhead);
+    st_issue = st1;  // slot 1's stage (slot 0 after the shift) is refilled next
+    __builtin_amdgcn_s_waitcnt(kWaitNext);  // this wave's loads of the next two units landed
+    wg_barrier();                           // ... and every wave's
+    // done when the stream is exhausted and no issued unit awaits its PV
+    return !(stream_done && (qval >> 1) == 0);
+  };
+  f32x16 sA = {}, sB = {};
+  while (iteration(sA, sB) && iteration(sB, sA)) {
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
 
   // ---- epilogue ----
-  const float lt = l + partner(l, g);
+  const float lt = l + partner_f(l, g);
   if (!qvalid) return;
   if (a.splits == 1) {
     const float inv = 1.f / lt;
@@ -396,78 +514,14 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fwd_kernel(FwdArgs a) {
   }
 }
 
-// Dense attention only: the sparse path runs fwd4_kernel.
 hipError_t launch_forward(const FwdArgs& a, bool sparse, int B, hipStream_t s) {
-  (void)B;
-  if (sparse) return hipErrorInvalidValue;
   const int grid = (a.total + 7) & ~7;
-  fwd_kernel<false, 128, 4><<<grid, 256, 0, s>>>(a);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Exact N-way merge of split partials (unnormalised numerator, max, denominator).
-// One workgroup of 128 threads per (head, row); thread = dimension.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
-  const int64_t rg = blockIdx.x;  // h * N + row
-  const int64_t HN = (int64_t)a.H * a.N;
-  const int d = threadIdx.x;
-  float M = -__builtin_inff();
-  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.part_ml[(s * HN + rg) * 2]);
-  const float mref = M == -__builtin_inff() ? 0.f : M;
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < a.splits; ++s) {
-    const float w = exp2f(a.part_ml[(s * HN + rg) * 2] - mref);
-    den += w * a.part_ml[(s * HN + rg) * 2 + 1];
-    num += w * a.part_o[(s * HN + rg) * kHeadDim + d];
-  }
-  a.out[rg * kHeadDim + d] = f32_to_bf16_bits(num / den);
-  if (d == 0 && a.lse) a.lse[rg] = mref * kLn2 + logf(den);
-}
-
-hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  combine_kernel<<<(unsigned)((int64_t)a.H * a.N), 128, 0, s>>>(a);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Two-way LSE merge (doubleAI page, "Attention across two GPUs").
-// 16 threads per row, 8 dimensions (16 bytes) each; the 16 threads of a row
-// sit in one wave, so a row is read before it is written when out aliases an
-// input.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t rg = gid >> 4;
-  const int c = (int)(gid & 15);
-  if (rg >= (int64_t)a.H * a.N) return;
-  const float la = a.lse_a[rg], lb = a.lse_b[rg];
-  const float M = fmaxf(la, lb);
-  float wa = 0.f, wb = 0.f, L = -__builtin_inff();
-  if (M != -__builtin_inff()) {
-    const float ea = expf(la - M), eb = expf(lb - M);
-    const float z = ea + eb;
-    L = M + logf(z);
-    wa = ea / z;
-    wb = eb / z;
-  }
-  const u32x4 xa = *reinterpret_cast<const u32x4*>(a.out_a + rg * kHeadDim + c * 8);
-  const u32x4 xb = *reinterpret_cast<const u32x4*>(a.out_b + rg * kHeadDim + c * 8);
-  u32x4 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float lo = wa * __uint_as_float(xa[e] << 16) + wb * __uint_as_float(xb[e] << 16);
-    const float hi = wa * __uint_as_float(xa[e] & 0xffff0000u) + wb * __uint_as_float(xb[e] & 0xffff0000u);
-    r[e] = (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
-  }
-  *reinterpret_cast<u32x4*>(a.out + rg * kHeadDim + c * 8) = r;
-  if (c == 0) a.lse[rg] = L;
-}
-
-hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
-  const int64_t threads = (int64_t)a.H * a.N * 16;
-  merge_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(a);
+  if (!sparse)
+    fwd_kernel<false, 128><<<grid, 256, 0, s>>>(a);
+  else if (B == 64)
+    fwd_kernel<true, 64><<<grid, 256, 0, s>>>(a);
+  else
+    fwd_kernel<true, 128><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

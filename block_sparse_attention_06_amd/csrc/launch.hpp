@@ -88,7 +88,6 @@ hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t s);
 hipError_t launch_forward(const FwdArgs& a, bool sparse, int B, hipStream_t s);
 hipError_t launch_forward_pp(const FwdArgs& a, bool sparse, int B, hipStream_t s);
-hipError_t launch_forward4(const FwdArgs& a, bool sparse, int B, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 

@@ -1,0 +1,78 @@
+// Exact merges of partial attention answers for gfx950: the N-way combine of
+// split-KV partials (unnormalised numerator, running max, denominator) and the
+// two-way LSE merge of finished (out, lse) pairs.
+//
+// doubleAI page, "Attention across two GPUs": partial answers over disjoint key
+// ranges, each carrying its log-sum-exp, merge exactly into the full answer.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace solattn {
+
+// ---------------------------------------------------------------------------
+// Exact N-way merge of split partials (unnormalised numerator, max, denominator).
+// One workgroup of 128 threads per (head, row); thread = dimension.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
+  const int64_t rg = blockIdx.x;  // h * N + row
+  const int64_t HN = (int64_t)a.H * a.N;
+  const int d = threadIdx.x;
+  float M = -__builtin_inff();
+  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.part_ml[(s * HN + rg) * 2]);
+  const float mref = M == -__builtin_inff() ? 0.f : M;
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < a.splits; ++s) {
+    const float w = exp2f(a.part_ml[(s * HN + rg) * 2] - mref);
+    den += w * a.part_ml[(s * HN + rg) * 2 + 1];
+    num += w * a.part_o[(s * HN + rg) * kHeadDim + d];
+  }
+  a.out[rg * kHeadDim + d] = f32_to_bf16_bits(num / den);
+  if (d == 0 && a.lse) a.lse[rg] = mref * kLn2 + logf(den);
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  combine_kernel<<<(unsigned)((int64_t)a.H * a.N), 128, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Two-way LSE merge (doubleAI page, "Attention across two GPUs").
+// 16 threads per row, 8 dimensions (16 bytes) each; the 16 threads of a row
+// sit in one wave, so a row is read before it is written when out aliases an
+// input.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rg = gid >> 4;
+  const int c = (int)(gid & 15);
+  if (rg >= (int64_t)a.H * a.N) return;
+  const float la = a.lse_a[rg], lb = a.lse_b[rg];
+  const float M = fmaxf(la, lb);
+  float wa = 0.f, wb = 0.f, L = -__builtin_inff();
+  if (M != -__builtin_inff()) {
+    const float ea = expf(la - M), eb = expf(lb - M);
+    const float z = ea + eb;
+    L = M + logf(z);
+    wa = ea / z;
+    wb = eb / z;
+  }
+  const u32x4 xa = *reinterpret_cast<const u32x4*>(a.out_a + rg * kHeadDim + c * 8);
+  const u32x4 xb = *reinterpret_cast<const u32x4*>(a.out_b + rg * kHeadDim + c * 8);
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float lo = wa * __uint_as_float(xa[e] << 16) + wb * __uint_as_float(xb[e] << 16);
+    const float hi = wa * __uint_as_float(xa[e] & 0xffff0000u) + wb * __uint_as_float(xb[e] & 0xffff0000u);
+    r[e] = (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  }
+  *reinterpret_cast<u32x4*>(a.out + rg * kHeadDim + c * 8) = r;
+  if (c == 0) a.lse[rg] = L;
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
+  const int64_t threads = (int64_t)a.H * a.N * 16;
+  merge_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace solattn

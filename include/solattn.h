@@ -54,6 +54,12 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden symbols by default; exactly the
+ * declarations below are exported. */
+#if defined(__GNUC__)
+#pragma GCC visibility push(default)
+#endif
+
 /* return codes */
 #define SOL_OK 0
 #define SOL_ERR_INVALID_ARG (-1) /* null pointer, size <= 0, NaN beta, short workspace, misalignment */
@@ -162,6 +168,10 @@ int sol_attn_block_mask(const uint16_t* q, const float* kbar, const float* mu,
                         const float* sigma, float beta, int row0, int nrows, int N,
                         int Nk, int H, int d, int B, uint8_t* mask, int64_t* counts,
                         void* stream);
+
+#if defined(__GNUC__)
+#pragma GCC visibility pop
+#endif
 
 #ifdef __cplusplus
 }
