@@ -334,6 +334,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     bf16x8 pb[2];
     float neg_ref = 0.f;
     if (pv) neg_ref = softmax_head(s_in, qkey[1], (qmine & 2u) != 0);
+    // The product-issuing part of the iteration runs at raised wave priority:
+    // when both waves of a SIMD are ready, the one feeding the matrix core
+    // issues first, and the other's bookkeeping fills the gaps.
+    __builtin_amdgcn_s_setprio(1);
     if (pv && do_s) {
       // The probabilities of slot 1 and the S products of slot 2 do not
       // depend on each other: interleave about six vector instructions after
@@ -350,6 +354,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       asm volatile("" : "=v"(s_out));  // unused: defined without an instruction
     }
     if (pv) mma_pv(st1, pb);
+    __builtin_amdgcn_s_setprio(0);
 
       // -- next unit of the stream --
       bool have = false;

@@ -162,6 +162,22 @@ def test_sparse_ragged_and_short_query():
     _sparse_case(Q, K, V, 64, 0.0)
 
 
+@pytest.mark.parametrize("N,Nk,B,beta", [
+    (3900, 3900, 128, 0.5),     # last query tile ragged
+    (4000, 3037, 64, 0.0),      # keys end inside a 32-key unit
+    (3968, 4100, 128, -0.3),    # query tiles end exactly on a tile
+    (4096, 4096, 64, INF),      # nothing selected: Taylor terms only
+    (3900, 2500, 128, -1e6),    # every block selected
+])
+def test_sparse_many_tiles(N, Nk, B, beta):
+    """Sixteen heads of ~4K rows: enough query tiles to fill the chip without a
+    key split, as long sequences run; checked on the first and last head, all
+    rows."""
+    H = 16
+    Q, K, V = gaussian(H, N, 128, seed=N + Nk + B, nk=Nk)
+    _sparse_case(Q, K, V, B, beta, heads=(0, H - 1))
+
+
 def test_sparse_split_keys_short_query():
     """Few query tiles: the sparse key range is split over workgroups (chunks of
     32 blocks) and merged; must match the unsplit oracle."""
