@@ -189,14 +189,20 @@ def main():
     step_ms = wall * 1e3 / args.steps
     log(f"step {step_ms:.3f} ms  self {np.median(self_ms):.3f} ms  cross {np.median(cross_ms):.3f} ms")
 
-    # routing kernels alone (same kernels as inside the call), to split the call
+    # routing kernels alone (same kernels as inside the call), to split the call;
+    # from 128 key blocks on the call computes the statistics in moment form
     nrep = max(3, args.steps)
     e = [torch.cuda.Event(enable_timing=True) for _ in range(3 * nrep)]
+    moment = (N + B - 1) // B >= 128
+    mws = torch.empty(H * (2 * 128 * 128 * 2 + 128 * 4), dtype=torch.uint8, device=q.device)
     for i in range(nrep):
         e[3 * i].record(stream)
         kb_, vb_ = sa.sol_attn_pool(k, v, B)
         e[3 * i + 1].record(stream)
-        mu, sigma = sa.sol_attn_row_stats(q, kb_, B, N)
+        if moment:
+            mu, sigma = sa.sol_attn_row_stats_moment(q, kb_, B, N, workspace=mws)
+        else:
+            mu, sigma = sa.sol_attn_row_stats(q, kb_, B, N)
         e[3 * i + 2].record(stream)
     torch.cuda.synchronize()
     pool_ms = float(np.median([e[3 * i].elapsed_time(e[3 * i + 1]) for i in range(nrep)]))

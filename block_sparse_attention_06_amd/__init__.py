@@ -27,6 +27,7 @@ __all__ = [
     "load_library",
     "sol_attn_pool",
     "sol_attn_row_stats",
+    "sol_attn_row_stats_moment",
     "sol_attn_forward",
     "sol_attn_workspace_size",
     "attn_lse_merge",
@@ -71,6 +72,7 @@ def load_library() -> ctypes.CDLL:
     sigs = {
         "sol_attn_pool": (I, [P, P, P, P, I, I, I, I, P]),
         "sol_attn_row_stats": (I, [P, P, P, P, I, I, I, I, I, P]),
+        "sol_attn_row_stats_moment": (I, [P, P, P, P, I, I, I, I, I, P, S, P]),
         "sol_attn_forward": (I, [P, P, P, P, P, I, I, I, I, F, I, I, P, S, P]),
         "sol_attn_workspace_size": (S, [I, I, I, I, I, I]),
         "attn_lse_merge": (I, [P, P, P, P, P, P, I, I, I, P]),
@@ -139,6 +141,26 @@ def sol_attn_row_stats(q: torch.Tensor, kbar: torch.Tensor, B: int, Nk: int, str
     sigma = torch.empty_like(mu)
     _check("sol_attn_row_stats", lib.sol_attn_row_stats(
         _ptr(q), _ptr(kbar), _ptr(mu), _ptr(sigma), N, int(Nk), H, d, int(B), _stream(stream)))
+    return mu, sigma
+
+
+def sol_attn_row_stats_moment(q: torch.Tensor, kbar: torch.Tensor, B: int, Nk: int,
+                              workspace: Optional[torch.Tensor] = None, stream=None):
+    """``(mu, sigma)`` as :func:`sol_attn_row_stats`, in moment form (the form the
+    forward pass uses from 128 key blocks on).  ``workspace`` (uint8, at least
+    ``H * (2*128*128*2 + 128*4)`` bytes) is allocated when not given."""
+    lib = load_library()
+    _want(q, "q", torch.bfloat16, 3)
+    _want(kbar, "kbar", torch.float32, 3)
+    H, N, d = q.shape
+    need = H * (2 * d * d * 2 + d * 4)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    mu = torch.empty((H, N), dtype=torch.float32, device=q.device)
+    sigma = torch.empty_like(mu)
+    _check("sol_attn_row_stats_moment", lib.sol_attn_row_stats_moment(
+        _ptr(q), _ptr(kbar), _ptr(mu), _ptr(sigma), N, int(Nk), H, d, int(B),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return mu, sigma
 
 

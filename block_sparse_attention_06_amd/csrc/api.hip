@@ -14,6 +14,10 @@ namespace {
 
 constexpr int kCUs = 256;            // MI355X compute units
 constexpr int kSplitTarget = 4 * kCUs;  // workgroups wanted before splitting keys stops
+// From this many key blocks on, the row statistics use the moment form (2 d^2
+// multiply-adds per row instead of 2 d nb).
+constexpr int kMomentMinBlocks = 128;
+constexpr size_t kMomentBytesPerHead = 2 * 128 * 128 * sizeof(uint16_t) + 128 * sizeof(float);
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -48,6 +52,8 @@ struct Plan {
   Split sp, dn;  // sparse plan (blocks of B) and dense plan (tiles of 128 keys)
   int max_splits;
   size_t off_kbar, off_vbar, off_vsum, off_khi, off_klo, off_mu, off_sigma, off_po, off_pml, bytes;
+  size_t off_chi, off_clo, off_mbar;  // moment-form statistics (nb >= kMomentMinBlocks)
+  bool moments;
 };
 
 // Sizes are validated by the caller.  A sparse-mode workspace also covers the
@@ -76,6 +82,12 @@ Plan make_plan(int N, int Nk, int H, int B, int mode) {
     p.off_klo = take((size_t)H * p.sp.nb_pad * 128 * sizeof(uint16_t));
     p.off_mu = take(HN * sizeof(float));
     p.off_sigma = take(HN * sizeof(float));
+    p.moments = p.sp.nb >= kMomentMinBlocks;
+    if (p.moments) {
+      p.off_chi = take((size_t)H * 128 * 128 * sizeof(uint16_t));
+      p.off_clo = take((size_t)H * 128 * 128 * sizeof(uint16_t));
+      p.off_mbar = take((size_t)H * 128 * sizeof(float));
+    }
   }
   if (p.max_splits > 1) {
     p.off_po = take((size_t)p.max_splits * HN * 128 * sizeof(float));
@@ -132,6 +144,24 @@ int sol_attn_row_stats(const uint16_t* q, const float* kbar, float* mu, float* s
   return hip_status(launch_stats(a, (hipStream_t)stream));
 }
 
+int sol_attn_row_stats_moment(const uint16_t* q, const float* kbar, float* mu, float* sigma,
+                              int N, int Nk, int H, int d, int B, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  if (!q || !kbar || !mu || !sigma || !workspace) return SOL_ERR_INVALID_ARG;
+  if (Nk == 0) Nk = N;
+  if (Nk < 0) return SOL_ERR_INVALID_ARG;
+  if (int r = check_shape(N, H, d)) return r;
+  if (int r = check_block(B)) return r;
+  if (!aligned(q, 16) || !aligned(kbar, 16) || !aligned(workspace, 256)) return SOL_ERR_INVALID_ARG;
+  if (ws_bytes < (size_t)H * kMomentBytesPerHead) return SOL_ERR_INVALID_ARG;
+  char* ws = (char*)workspace;
+  MomentArgs ma{kbar, (uint16_t*)ws, (uint16_t*)(ws + (size_t)H * 128 * 128 * sizeof(uint16_t)),
+                (float*)(ws + (size_t)H * 2 * 128 * 128 * sizeof(uint16_t)), H, cdiv(Nk, B)};
+  if (int r = hip_status(launch_moments(ma, (hipStream_t)stream))) return r;
+  StatsMomentArgs sm{q, ma.chi, ma.clo, ma.mbar, mu, sigma, N, H};
+  return hip_status(launch_stats_moment(sm, (hipStream_t)stream));
+}
+
 size_t sol_attn_workspace_size(int N, int Nk, int H, int d, int B, int mode) {
   if (Nk == 0) Nk = N;
   if (N <= 0 || Nk <= 0 || H <= 0 || d != 128) return 0;
@@ -174,9 +204,19 @@ int sol_attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, ui
                 (uint16_t*)(ws + p.off_vsum), (uint16_t*)(ws + p.off_khi),
                 (uint16_t*)(ws + p.off_klo), Nk, H, B, sp.nb, sp.nb_pad};
     if (int r = hip_status(launch_pool(pa, s))) return r;
-    StatsArgs sa{q, pa.kbar, (float*)(ws + p.off_mu), (float*)(ws + p.off_sigma), N, H, sp.nb};
-    if (int r = hip_status(launch_stats(sa, s))) return r;
-    f.khi = pa.khi; f.klo = pa.klo; f.vsumT = pa.vsumT; f.mu = sa.mu; f.sigma = sa.sigma;
+    float* mu = (float*)(ws + p.off_mu);
+    float* sigma = (float*)(ws + p.off_sigma);
+    if (p.moments) {
+      MomentArgs ma{pa.kbar, (uint16_t*)(ws + p.off_chi), (uint16_t*)(ws + p.off_clo),
+                    (float*)(ws + p.off_mbar), H, sp.nb};
+      if (int r = hip_status(launch_moments(ma, s))) return r;
+      StatsMomentArgs sm{q, ma.chi, ma.clo, ma.mbar, mu, sigma, N, H};
+      if (int r = hip_status(launch_stats_moment(sm, s))) return r;
+    } else {
+      StatsArgs sa{q, pa.kbar, mu, sigma, N, H, sp.nb};
+      if (int r = hip_status(launch_stats(sa, s))) return r;
+    }
+    f.khi = pa.khi; f.klo = pa.klo; f.vsumT = pa.vsumT; f.mu = mu; f.sigma = sigma;
   }
   if (f.splits > 1) {
     f.part_o = (float*)(ws + p.off_po);

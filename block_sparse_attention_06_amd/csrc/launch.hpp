@@ -25,6 +25,26 @@ struct StatsArgs {
   int N, H, nb;
 };
 
+// Moment form of the row statistics: mbar = mean_j kbar_j and the covariance
+// C = mean_j (kbar_j - mbar)(kbar_j - mbar)^T of the pooled keys, per head.
+struct MomentArgs {
+  const float* kbar;  // [H, nb, 128]
+  uint16_t* chi;      // [H, 128, 128] bf16 hi part of C, rows permuted for the MFMA A operand
+  uint16_t* clo;      // [H, 128, 128] bf16 lo part
+  float* mbar;        // [H, 128]
+  int H, nb;
+};
+
+struct StatsMomentArgs {
+  const uint16_t* q;
+  const uint16_t* chi;
+  const uint16_t* clo;
+  const float* mbar;
+  float* mu;
+  float* sigma;
+  int N, H;
+};
+
 struct ProxyArgs {
   const uint16_t* q;
   const float* kbar;
@@ -84,6 +104,8 @@ struct MergeArgs {
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 hipError_t launch_stats(const StatsArgs& a, hipStream_t s);
+hipError_t launch_moments(const MomentArgs& a, hipStream_t s);
+hipError_t launch_stats_moment(const StatsMomentArgs& a, hipStream_t s);
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t s);
 hipError_t launch_forward(const FwdArgs& a, bool sparse, int B, hipStream_t s);

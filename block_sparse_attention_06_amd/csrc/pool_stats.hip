@@ -165,6 +165,152 @@ hipError_t launch_stats(const StatsArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Row statistics in moment form.  p_ij - mu_i = s q_i . (kbar_j - mbar) is
+// linear in q_i, so over the blocks
+//   mu_i = s q_i . mbar,   sigma_i^2 = s^2 q_i^T C q_i,
+// with mbar the mean of the pooled keys and C their covariance (population,
+// centred, so no cancellation).  Same quantities as stats_kernel up to
+// rounding, at 2 d^2 instead of 2 d nb multiply-adds per row.
+//
+// moments_kernel: one workgroup per (16 rows of C, head).  The mean is summed
+// by all 256 threads (two per dimension), then 32 centred pooled keys at a
+// time are staged in LDS and each thread accumulates 8 entries of C in fp32.
+// C is written as bf16 hi + lo parts (~16 significant bits), rows permuted
+// (see c_row_pos) so that stats_moment_kernel's accumulator elements line up
+// with its query fragment.
+// ---------------------------------------------------------------------------
+
+// Stored position, within its 32-row tile, of row `off` of C.  The MFMA
+// accumulator element e of lane half g sits in row 8(e/4) + 4g + e%4 of the
+// tile; storing C row 16(b/2) + 8g + 4(b%2) + i (b = e/4, i = e%4) there makes
+// element e of lane half g the query dimension that element e % 8 of query
+// fragment k-step 2 tile + e / 8 holds in that lane half.
+__device__ __forceinline__ int c_row_pos(int off) {
+  return 8 * (2 * (off >> 4) + ((off >> 2) & 1)) + 4 * ((off >> 3) & 1) + (off & 3);
+}
+
+__global__ __launch_bounds__(256) void moments_kernel(MomentArgs a) {
+  __shared__ float kc[kChunk][kHeadDim + 4];
+  __shared__ float part[2][kHeadDim];
+  const int rb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const float* kb = a.kbar + (int64_t)h * a.nb * kHeadDim;
+  {
+    const int dim = tid & (kHeadDim - 1), par = tid >> 7;
+    float acc = 0.f;
+    for (int j = par; j < a.nb; j += 2) acc += kb[(int64_t)j * kHeadDim + dim];
+    part[par][dim] = acc;
+  }
+  __syncthreads();
+  const float inv_nb = 1.f / (float)a.nb;
+  const int r = rb * 16 + (tid >> 4), c0 = (tid & 15) * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < a.nb; j0 += kChunk) {
+    __syncthreads();  // the previous chunk has been consumed
+    for (int e = tid; e < kChunk * kHeadDim; e += 256) {
+      const int rr = e >> 7, cc = e & (kHeadDim - 1), j = j0 + rr;
+      const float mean = (part[0][cc] + part[1][cc]) * inv_nb;
+      kc[rr][cc] = j < a.nb ? kb[(int64_t)j * kHeadDim + cc] - mean : 0.f;
+    }
+    __syncthreads();
+    const int nj = min(kChunk, a.nb - j0);
+    for (int jj = 0; jj < nj; ++jj) {
+      const float x = kc[jj][r];
+      const f32x4 y0 = *reinterpret_cast<const f32x4*>(&kc[jj][c0]);
+      const f32x4 y1 = *reinterpret_cast<const f32x4*>(&kc[jj][c0 + 4]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[k] = __builtin_fmaf(x, y0[k], acc[k]);
+        acc[k + 4] = __builtin_fmaf(x, y1[k], acc[k + 4]);
+      }
+    }
+  }
+  bf16x8 hi, lo;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    __bf16 hh, ll;
+    split_bf16(acc[k] * inv_nb, hh, ll);
+    hi[k] = hh;
+    lo[k] = ll;
+  }
+  const int64_t pos = ((int64_t)h * kHeadDim + (r & ~31) + c_row_pos(r & 31)) * kHeadDim + c0;
+  *reinterpret_cast<bf16x8*>(a.chi + pos) = hi;
+  *reinterpret_cast<bf16x8*>(a.clo + pos) = lo;
+  if (rb == 0 && tid < kHeadDim) a.mbar[(int64_t)h * kHeadDim + tid] = (part[0][tid] + part[1][tid]) * inv_nb;
+}
+
+hipError_t launch_moments(const MomentArgs& a, hipStream_t s) {
+  moments_kernel<<<dim3(kHeadDim / 16, a.H), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// stats_moment_kernel: one wave per 32 query rows, four per workgroup.  C (hi
+// and lo, 64 KiB) is staged in LDS (16-byte chunk c of row R at c ^ (R % 16));
+// Y^T = C Q^T runs on MFMA as 4 row tiles x 8 k-steps x (hi, lo), then each
+// lane dots its 64 accumulator elements with the matching query values, which
+// it already holds as MFMA operands, and adds the partner lane's half.
+__global__ __launch_bounds__(256) void stats_moment_kernel(StatsMomentArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 chs[kHeadDim * kHeadDim];
+  __shared__ __attribute__((aligned(16))) u16 cls[kHeadDim * kHeadDim];
+  __shared__ float mb[kHeadDim];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+  const int h = blockIdx.y;
+  const int row = blockIdx.x * kQTile + wave * 32 + (lane & 31);
+  const bool valid = row < a.N;
+  const u16* ch = a.chi + (int64_t)h * kHeadDim * kHeadDim;
+  const u16* cl = a.clo + (int64_t)h * kHeadDim * kHeadDim;
+  for (int e = tid; e < kHeadDim * 16; e += 256) {
+    const int R = e >> 4, c = e & 15;
+    const u32x4 xh = gload<u32x4>(ch + R * kHeadDim + c * 8);
+    const u32x4 xl = gload<u32x4>(cl + R * kHeadDim + c * 8);
+    const int off = R * kHeadDim + ((c ^ (R & 15)) << 3);
+    *reinterpret_cast<u32x4*>(&chs[off]) = xh;
+    *reinterpret_cast<u32x4*>(&cls[off]) = xl;
+  }
+  if (tid < kHeadDim) mb[tid] = a.mbar[(int64_t)h * kHeadDim + tid];
+  QFrag qf;
+  load_qfrag(qf, a.q + (int64_t)h * a.N * kHeadDim, row, valid, g);
+  __syncthreads();
+  const int r = lane & 31;
+  f32x16 y[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    y[ct] = f32x16{};
+    const int R = ct * 32 + r;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int off = R * kHeadDim + (((ks * 2 + g) ^ (R & 15)) << 3);
+      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(&chs[off]);
+      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(&cls[off]);
+      y[ct] = mfma32(hi, qf.k[ks], y[ct]);
+      y[ct] = mfma32(lo, qf.k[ks], y[ct]);
+    }
+  }
+  float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      s2 = __builtin_fmaf(y[ct][e], (float)qf.k[2 * ct + (e >> 3)][e & 7], s2);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s1 = __builtin_fmaf((float)qf.k[ks][k], mb[16 * ks + 8 * g + k], s1);
+  s1 += __shfl_xor(s1, 32);
+  s2 += __shfl_xor(s2, 32);
+  if (g == 0 && valid) {
+    const float scale = 0.08838834764831845f;  // 1/sqrt(128)
+    a.mu[(int64_t)h * a.N + row] = s1 * scale;
+    a.sigma[(int64_t)h * a.N + row] = sqrtf(fmaxf(s2, 0.f)) * scale;
+  }
+}
+
+hipError_t launch_stats_moment(const StatsMomentArgs& a, hipStream_t s) {
+  dim3 grid((a.N + kQTile - 1) / kQTile, a.H);
+  stats_moment_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Inspection: proxy scores of a row range.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void proxy_kernel(ProxyArgs a) {

@@ -98,6 +98,23 @@ int sol_attn_row_stats(const uint16_t* q, const float* kbar, float* mu, float* s
                        int N, int Nk, int H, int d, int B, void* stream);
 
 /*
+ * The same statistics in moment form, as sol_attn_forward computes them from
+ * 128 key blocks on: p_ij - mu_i = q_i . (kbar_j - mbar) / sqrt(d) is linear
+ * in q_i, so mu_i = q_i . mbar / sqrt(d) and sigma_i^2 = q_i^T C q_i / d, with
+ * mbar the mean and C the population covariance of the pooled keys of a head.
+ * Equal to sol_attn_row_stats up to rounding, at 2 d^2 instead of 2 d nb
+ * multiply-adds per row.
+ * Arguments as sol_attn_row_stats, plus:
+ * workspace  device scratch of at least H * (2 * d * d * 2 + d * 4) bytes,
+ *            256-byte aligned, caller-owned; it holds mbar and C (bf16 hi and
+ *            lo parts) on return.
+ * ws_bytes   its size; smaller returns SOL_ERR_INVALID_ARG before any launch.
+ */
+int sol_attn_row_stats_moment(const uint16_t* q, const float* kbar, float* mu, float* sigma,
+                              int N, int Nk, int H, int d, int B, void* workspace,
+                              size_t ws_bytes, void* stream);
+
+/*
  * Attention forward.
  *   SOL_SPARSE: Sol-Engine LTX25 page, "Stage 2 Optimization -- Core
  *   Technology: Sol-Attn" (all three bullets), with the Taylor weight above.

@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("sol_attn_pool", "sol_attn_forward", "attn_lse_merge", "sol_attn_row_stats",
-              "sol_attn_workspace_size", "sol_attn_error_string", "sol_attn_proxy_scores",
+              "sol_attn_row_stats_moment", "sol_attn_workspace_size", "sol_attn_error_string", "sol_attn_proxy_scores",
               "sol_attn_block_mask"):
         assert n in names
 
@@ -78,6 +78,11 @@ def test_other_entry_points_argument_errors(lib):
     assert lib.sol_attn_pool(FAKE, FAKE, FAKE, FAKE, 64, 1, 96, 64, N) == -2
     assert lib.sol_attn_pool(FAKE, FAKE, FAKE, FAKE, 64, 1, 128, 100, N) == -2
     assert lib.sol_attn_row_stats(FAKE, N, FAKE, FAKE, 64, 64, 1, 128, 64, N) == -1
+    need = 2 * 128 * 128 * 2 + 128 * 4  # one head
+    rsm = lib.sol_attn_row_stats_moment
+    assert rsm(FAKE, FAKE, FAKE, FAKE, 64, 64, 1, 128, 64, N, need, N) == -1      # no workspace
+    assert rsm(FAKE, FAKE, FAKE, FAKE, 64, 64, 1, 128, 64, FAKE, need - 1, N) == -1  # too small
+    assert rsm(FAKE, FAKE, FAKE, FAKE, 64, 64, 1, 96, 64, FAKE, need, N) == -2
     assert lib.attn_lse_merge(FAKE, FAKE, FAKE, FAKE, FAKE, N, 64, 1, 128, N) == -1
     assert lib.attn_lse_merge(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 128, N) == -1
     assert lib.sol_attn_proxy_scores(FAKE, FAKE, FAKE, 60, 10, 64, 64, 1, 128, 64, N) == -1

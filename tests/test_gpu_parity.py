@@ -70,6 +70,25 @@ def test_proxy_and_stats_parity(case):
         assert np.abs(host(sigma[h]) - sr).max() < 2e-5
 
 
+@pytest.mark.parametrize("H,N,B", [(2, 2048, 64), (2, 1500, 128), (2, 20000, 128), (1, 130, 64)])
+def test_row_stats_moment_parity(H, N, B):
+    """Moment form (mean and covariance of the pooled keys) against the oracle's
+    statistics of the proxy scores, and against the direct form on the GPU."""
+    Q, K, V = gaussian(H, N, 128, seed=60 + N)
+    q = dev(Q)
+    kbar, _ = sa.sol_attn_pool(dev(K), dev(V), B)
+    mu, sigma = sa.sol_attn_row_stats_moment(q, kbar, B, N)
+    mu_d, sigma_d = sa.sol_attn_row_stats(q, kbar, B, N)
+    torch.cuda.synchronize()
+    for h in range(H):
+        kb = O.pool_ref(_head(K, h), B)
+        mr, sr = O.row_stats_ref(O.proxy_ref(_head(Q, h), kb))
+        assert np.abs(host(mu[h]) - mr).max() < 2e-5
+        assert np.abs(host(sigma[h]) - sr).max() < 2e-5
+    assert (mu - mu_d).abs().max().item() < 4e-5
+    assert (sigma - sigma_d).abs().max().item() < 4e-5
+
+
 @pytest.mark.parametrize("beta", [0.0, 0.5, 1.0, -0.5])
 def test_block_mask_parity(beta):
     w = WORKLOADS["tiny"]
