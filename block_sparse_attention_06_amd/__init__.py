@@ -34,6 +34,8 @@ __all__ = [
     "sol_attn_error_string",
     "sol_attn_proxy_scores",
     "sol_attn_block_mask",
+    "fp8_quantize_rows",
+    "fp8_gemm_rowscale",
 ]
 
 SOL_DENSE = 0
@@ -69,6 +71,7 @@ def load_library() -> ctypes.CDLL:
             "(there is no fallback implementation)")
     lib = ctypes.CDLL(path)
     P, I, F, S, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_char_p
+    L = ctypes.c_int64
     sigs = {
         "sol_attn_pool": (I, [P, P, P, P, I, I, I, I, P]),
         "sol_attn_row_stats": (I, [P, P, P, P, I, I, I, I, I, P]),
@@ -79,6 +82,8 @@ def load_library() -> ctypes.CDLL:
         "sol_attn_error_string": (Z, [I]),
         "sol_attn_proxy_scores": (I, [P, P, P, I, I, I, I, I, I, I, P]),
         "sol_attn_block_mask": (I, [P, P, P, P, F, I, I, I, I, I, I, I, P, P, P]),
+        "fp8_quantize_rows": (I, [P, P, P, L, I, P]),
+        "fp8_gemm_rowscale": (I, [P, P, P, P, P, I, I, I, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -258,3 +263,37 @@ def sol_attn_block_mask(q: torch.Tensor, kbar: torch.Tensor, mu: torch.Tensor,
         _ptr(q), _ptr(kbar), _ptr(mu), _ptr(sigma), float(beta), int(row0), int(nrows), N,
         int(Nk), H, d, int(B), _ptr(mask), _ptr(counts), _stream(stream)))
     return mask, counts
+
+
+def fp8_quantize_rows(x: torch.Tensor, stream=None):
+    """Per-row E4M3 quantisation of a bf16 ``[M, K]`` matrix: returns
+    ``(codes [M, K] uint8, scale [M] fp32)`` with ``x ~ scale[:, None] * dec(codes)``."""
+    lib = load_library()
+    _want(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check("fp8_quantize_rows", lib.fp8_quantize_rows(_ptr(x), _ptr(q), _ptr(scale), M, K,
+                                                      _stream(stream)))
+    return q, scale
+
+
+def fp8_gemm_rowscale(a: torch.Tensor, sa: torch.Tensor, w: torch.Tensor, sw: torch.Tensor,
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """``y [M, N] bf16 = sa[:, None] * sw[None, :] * (dec(a) @ dec(w).T)`` with E4M3
+    codes ``a [M, K]``, ``w [N, K]`` (uint8) and fp32 accumulation."""
+    lib = load_library()
+    _want(a, "a", torch.uint8, 2)
+    _want(w, "w", torch.uint8, 2)
+    _want(sa, "sa", torch.float32, 1)
+    _want(sw, "sw", torch.float32, 1)
+    M, K = a.shape
+    N = w.shape[0]
+    if w.shape[1] != K or sa.shape[0] != M or sw.shape[0] != N:
+        raise ValueError("fp8_gemm_rowscale: shape mismatch")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _want(out, "out", torch.bfloat16, 2)
+    _check("fp8_gemm_rowscale", lib.fp8_gemm_rowscale(_ptr(a), _ptr(sa), _ptr(w), _ptr(sw),
+                                                      _ptr(out), M, N, K, _stream(stream)))
+    return out

@@ -162,6 +162,26 @@ int sol_attn_row_stats_moment(const uint16_t* q, const float* kbar, float* mu, f
   return hip_status(launch_stats_moment(sm, (hipStream_t)stream));
 }
 
+int fp8_quantize_rows(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int K,
+                      void* stream) {
+  if (!x || !q || !scale || M <= 0 || K <= 0) return SOL_ERR_INVALID_ARG;
+  if (K % 8 != 0) return SOL_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(q, 8)) return SOL_ERR_INVALID_ARG;
+  Fp8QuantArgs a{x, q, scale, M, K};
+  return hip_status(launch_quantize_rows(a, (hipStream_t)stream));
+}
+
+int fp8_gemm_rowscale(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                      uint16_t* y, int M, int N, int K, void* stream) {
+  if (!a || !sa || !w || !sw || !y || M <= 0 || N <= 0 || K <= 0) return SOL_ERR_INVALID_ARG;
+  if (K % 128 != 0 || N % 128 != 0) return SOL_ERR_UNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(sw, 16) || !aligned(y, 16))
+    return SOL_ERR_INVALID_ARG;
+  Fp8GemmArgs g{};
+  g.a = a; g.sa = sa; g.w = w; g.sw = sw; g.y = y; g.M = M; g.N = N; g.K = K;
+  return hip_status(launch_fp8_gemm(g, (hipStream_t)stream));
+}
+
 size_t sol_attn_workspace_size(int N, int Nk, int H, int d, int B, int mode) {
   if (Nk == 0) Nk = N;
   if (N <= 0 || Nk <= 0 || H <= 0 || d != 128) return 0;

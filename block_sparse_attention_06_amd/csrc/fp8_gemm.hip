@@ -1,0 +1,239 @@
+// FP8 projection GEMM for gfx950: activations quantised to E4M3 with one scale
+// per row, weights in E4M3 with one scale per output channel, products on the
+// FP8 matrix cores with FP32 accumulation, output bf16.
+//
+// [DAI] "LTX-2.5 at 4K, in half the time" (doubleAI), section "Thinner seams":
+// the refinement pass keeps its weights in FP8, converts the activations to FP8
+// with a separate scale for each row and accumulates in FP32, so the matrix
+// units run at their FP8 rate.
+//
+//   quantize_rows_kernel:  s_i = amax_i / 448,  q_ik = RNE_e4m3(x_ik * (448 / amax_i))
+//   fp8_gemm_kernel:       y_in = s_i * sw_n * sum_k dec(q_ik) dec(w_nk)   (bf16)
+//
+// v_mfma_f32_32x32x64_f8f6f4 with E4M3 operands (checked on gfx950 with an
+// in-bounds probe): lane l supplies row l % 32 of A (column l % 32 of B) with
+// 32 of the 64 k values, lane half l / 32 taking bytes [32 (l / 32), +32) of
+// the k slice; the accumulator layout is that of the bf16 32x32 MFMA (lane l
+// holds column l % 32, rows 8(i/4) + 4(l/32) + i%4).  Both operands are read
+// K-contiguous, so neither needs a transpose.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace solattn {
+
+namespace {
+
+constexpr float kE4m3Max = 448.f;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Row quantisation.  One wave per row, 8 bf16 (16 bytes) per lane per step:
+// pass 1 finds the row's absolute maximum, pass 2 (reading the row again, now
+// from cache) scales, clamps to +-448 (a scaled maximum may land one float32
+// ulp above it) and converts pairs with v_cvt_pk_fp8_f32 (round to nearest
+// even).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quantize_rows_kernel(Fp8QuantArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.M) return;
+  const u16* x = a.x + row * a.K;
+  float amax = 0.f;
+  for (int k = lane * 8; k < a.K; k += 512) {
+    const u32x4 v = gload<u32x4>(x + k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      amax = fmaxf(amax, fabsf(__uint_as_float(v[e] << 16)));
+      amax = fmaxf(amax, fabsf(__uint_as_float(v[e] & 0xFFFF0000u)));
+    }
+  }
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) amax = fmaxf(amax, __shfl_xor(amax, sh));
+  const float inv = amax > 0.f ? kE4m3Max / amax : 0.f;
+  if (lane == 0) a.scale[row] = amax / kE4m3Max;
+  uint8_t* q = a.q + row * a.K;
+  for (int k = lane * 8; k < a.K; k += 512) {
+    const u32x4 v = gload<u32x4>(x + k);
+    u32x2 out;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        f[2 * e] = __uint_as_float(v[2 * h + e] << 16) * inv;
+        f[2 * e + 1] = __uint_as_float(v[2 * h + e] & 0xFFFF0000u) * inv;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = fminf(fmaxf(f[e], -kE4m3Max), kE4m3Max);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w, true);
+      out[h] = (uint32_t)w;
+    }
+    *reinterpret_cast<u32x2*>(q + k) = out;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMM.  Workgroup: 4 waves on a 256 (tokens) x 256 (channels) output tile;
+// wave (wm, wn) owns 128 x 128 as 4 x 4 MFMA tiles computed transposed
+// (D = W A^T: lane l holds token l % 32 and, per tile, channels in groups of
+// four consecutive ones, so each store writes 8 contiguous bytes).
+// K streams through a four-stage LDS ring in slices of 64 bytes per row
+// (16 KiB of tokens + 16 KiB of weights per stage), filled by direct
+// global->LDS loads three slices ahead.  A row's four 16-byte chunks sit at
+// chunk c ^ ((row / 4) % 4), so the 16 lanes of each read phase hit 16
+// distinct bank groups.
+// ---------------------------------------------------------------------------
+constexpr int kGT = 256;              // tile edge (tokens and channels)
+constexpr int kGK = 64;               // K bytes per stage
+constexpr int kGStages = 4;
+constexpr int kGStageBytes = kGT * kGK;  // per operand
+constexpr int kGDmaPerStage = 8;         // per wave: 4 token + 4 weight instructions
+
+__device__ __forceinline__ int g_chunk(int row, int c) { return c ^ ((row >> 2) & 3); }
+
+__device__ __forceinline__ void g_dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(Fp8GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[kGStages][kGStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_w[kGStages][kGStageBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // XCD-aware order: workgroup b runs on XCD b % 8; the tiles of one XCD are
+  // consecutive in (token tile, channel tile) order, channel tile fastest, so
+  // the channel tiles of one token tile share that XCD's L2.
+  const int per_xcd = a.grid / 8;
+  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (logical >= a.tiles_m * a.tiles_n) return;
+  const int tm = logical / a.tiles_n, tn = logical % a.tiles_n;
+  const int m0 = tm * kGT, n0 = tn * kGT;
+  const int K = a.K;
+
+  // direct loads: instruction i of this wave fills rows 16 (4 wave + i) .. +15
+  // of a stage; lane l lands in row + l / 4, chunk slot l % 4
+  const uint8_t* abase[4];
+  const uint8_t* wbase[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave * 4 + i) * 16 + (lane >> 2);
+    const int c = g_chunk(r, lane & 3);
+    // rows past the end re-read the last row (finite data, never stored)
+    const int ra = min(m0 + r, a.M - 1), rw = min(n0 + r, a.N - 1);
+    abase[i] = a.a + (int64_t)ra * K + c * 16;
+    wbase[i] = a.w + (int64_t)rw * K + c * 16;
+  }
+  auto dma_stage = [&](int ks, int st) __attribute__((always_inline)) {
+    const int64_t k0 = (int64_t)ks * kGK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r0 = (wave * 4 + i) * 16;
+      g_dma16(abase[i] + k0, lds_addr(&lds_a[st][r0 * kGK]));
+      g_dma16(wbase[i] + k0, lds_addr(&lds_w[st][r0 * kGK]));
+    }
+  };
+
+  // operand reads: 32 bytes of row R (chunks 2g, 2g+1)
+  auto frag = [&](const uint8_t* base, int R) __attribute__((always_inline)) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + R * kGK + (g_chunk(R, 2 * g) << 4));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + R * kGK + (g_chunk(R, 2 * g + 1) << 4));
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  const int nk = K / kGK;
+#pragma unroll
+  for (int s = 0; s < kGStages - 1; ++s)
+    if (s < nk) dma_stage(s, s);
+
+  for (int ks = 0; ks < nk; ++ks) {
+    // this wave's loads of slice ks have landed once at most the loads of the
+    // younger slices already issued are outstanding
+    const int younger = min(kGStages - 2, nk - 1 - ks);
+    if (younger >= 2)
+      __builtin_amdgcn_s_waitcnt((2 * kGDmaPerStage & 15) | (((2 * kGDmaPerStage) >> 4) << 14) | 0x0F70);
+    else if (younger == 1)
+      __builtin_amdgcn_s_waitcnt((kGDmaPerStage & 15) | ((kGDmaPerStage >> 4) << 14) | 0x0F70);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (ks + kGStages - 1 < nk) dma_stage(ks + kGStages - 1, (ks + kGStages - 1) % kGStages);
+    const int st = ks % kGStages;
+    const uint8_t* sa_ = lds_a[st];
+    const uint8_t* sw_ = lds_w[st];
+    i32x8 bt[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) bt[mt] = frag(sa_, wm * 128 + mt * 32 + r32);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const i32x8 at = frag(sw_, wn * 128 + nt * 32 + r32);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma_fp8(at, bt[mt], acc[mt][nt]);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // epilogue: y[m][n] = acc * sa[m] * sw[n], bf16; lane holds token m and, per
+  // tile, channels n0 + 32 nt + 8 b + 4 g + (0..3) for b = 0..3
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int m = m0 + wm * 128 + mt * 32 + r32;
+    if (m >= a.M) continue;
+    const float sm = a.sa[m];
+    uint16_t* yrow = a.y + (int64_t)m * a.N;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int nb = n0 + wn * 128 + nt * 32;
+      if (nb >= a.N) continue;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int n = nb + 8 * b + 4 * g;
+        const f32x4v swv = gload<f32x4v>(a.sw + n);
+        u32x2 pk;
+        pk[0] = (uint32_t)f32_to_bf16_bits(acc[mt][nt][4 * b] * sm * swv[0]) |
+                ((uint32_t)f32_to_bf16_bits(acc[mt][nt][4 * b + 1] * sm * swv[1]) << 16);
+        pk[1] = (uint32_t)f32_to_bf16_bits(acc[mt][nt][4 * b + 2] * sm * swv[2]) |
+                ((uint32_t)f32_to_bf16_bits(acc[mt][nt][4 * b + 3] * sm * swv[3]) << 16);
+        *reinterpret_cast<u32x2*>(yrow + n) = pk;
+      }
+    }
+  }
+}
+
+hipError_t launch_quantize_rows(const Fp8QuantArgs& a, hipStream_t s) {
+  const int64_t blocks = (a.M + 3) / 4;
+  quantize_rows_kernel<<<(unsigned)blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_gemm(const Fp8GemmArgs& a0, hipStream_t s) {
+  Fp8GemmArgs a = a0;
+  a.tiles_m = (a.M + kGT - 1) / kGT;
+  a.tiles_n = (a.N + kGT - 1) / kGT;
+  a.grid = (a.tiles_m * a.tiles_n + 7) & ~7;
+  fp8_gemm_kernel<<<a.grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace solattn

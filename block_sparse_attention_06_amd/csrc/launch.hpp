@@ -45,6 +45,24 @@ struct StatsMomentArgs {
   int N, H;
 };
 
+struct Fp8QuantArgs {
+  const uint16_t* x;  // [M, K] bf16
+  uint8_t* q;         // [M, K] E4M3
+  float* scale;       // [M]
+  int64_t M;
+  int K;
+};
+
+struct Fp8GemmArgs {
+  const uint8_t* a;   // [M, K] E4M3 activations
+  const float* sa;    // [M]
+  const uint8_t* w;   // [N, K] E4M3 weights
+  const float* sw;    // [N]
+  uint16_t* y;        // [M, N] bf16
+  int M, N, K;
+  int tiles_m, tiles_n, grid;  // set by the launcher
+};
+
 struct ProxyArgs {
   const uint16_t* q;
   const float* kbar;
@@ -112,5 +130,7 @@ hipError_t launch_forward(const FwdArgs& a, bool sparse, int B, hipStream_t s);
 hipError_t launch_forward_pp(const FwdArgs& a, bool sparse, int B, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_quantize_rows(const Fp8QuantArgs& a, hipStream_t s);
+hipError_t launch_fp8_gemm(const Fp8GemmArgs& a, hipStream_t s);
 
 }  // namespace solattn

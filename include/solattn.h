@@ -186,6 +186,36 @@ int sol_attn_block_mask(const uint16_t* q, const float* kbar, const float* mu,
                         int Nk, int H, int d, int B, uint8_t* mask, int64_t* counts,
                         void* stream);
 
+/*
+ * FP8 projection GEMM around attention: weights stay in FP8, activations are
+ * converted to FP8 with one scale per row, products accumulate in FP32.
+ *   [DAI] "LTX-2.5 at 4K, in half the time" (doubleAI), section "Thinner seams".
+ * FP8 is E4M3 in its finite-only form (bias 7, largest finite value 448).
+ *
+ * fp8_quantize_rows: per-row quantisation of a bf16 matrix.
+ * x      [M, K] bf16 row-major (read), finite values; 16-byte aligned.
+ * q      [M, K] E4M3 codes (written): q_ik = RNE(x_ik * (448 / amax_i)), the
+ *        product formed in fp32 and clamped to +-448; 8-byte aligned.
+ * scale  [M] fp32 (written): amax_i / 448 (0 for an all-zero row, whose codes
+ *        are 0).
+ * K must be a multiple of 8 (SOL_ERR_UNSUPPORTED otherwise).
+ */
+int fp8_quantize_rows(const uint16_t* x, uint8_t* q, float* scale, int64_t M, int K,
+                      void* stream);
+
+/*
+ * fp8_gemm_rowscale: y[m, n] = sa[m] * sw[n] * sum_k dec(a[m, k]) * dec(w[n, k]),
+ * accumulated in fp32 on the FP8 matrix cores, written as bf16 (round to
+ * nearest even).
+ * a    [M, K] E4M3 activations (read), sa [M] fp32 their row scales.
+ * w    [N, K] E4M3 weights, one row per output channel (read), sw [N] fp32.
+ * y    [M, N] bf16 (written).
+ * K and N must be multiples of 128 (SOL_ERR_UNSUPPORTED otherwise); a, w, sw
+ * and y 16-byte aligned.  No workspace; nothing is allocated.
+ */
+int fp8_gemm_rowscale(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                      uint16_t* y, int M, int N, int K, void* stream);
+
 #if defined(__GNUC__)
 #pragma GCC visibility pop
 #endif

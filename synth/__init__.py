@@ -177,3 +177,23 @@ def gaussian(heads: int, n: int, d: int, seed: int, nk: Optional[int] = None,
         K[h] = f32_to_bf16_bits(np.float32(scale) * rng.standard_normal((nk, d), dtype=np.float32))
         V[h] = f32_to_bf16_bits(rng.standard_normal((nk, d), dtype=np.float32))
     return Q, K, V
+
+
+def activations(m: int, k: int, seed: int) -> np.ndarray:
+    """bf16 bits ``[m, k]`` of projection inputs: N(0, 1) rows, each row scaled
+    by its own power of two in [2^-6, 2^6], and a few channels 8x larger than
+    the rest (the outlier channels of transformer activations)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0xF8]))
+    x = rng.standard_normal((m, k), dtype=np.float32)
+    x *= np.exp2(rng.integers(-6, 7, (m, 1))).astype(np.float32)
+    x[:, rng.choice(k, size=max(1, k // 256), replace=False)] *= np.float32(8)
+    return f32_to_bf16_bits(x)
+
+
+def e4m3_codes(m: int, k: int, seed: int) -> np.ndarray:
+    """Uniformly random E4M3 byte codes ``[m, k]``, the two NaN patterns
+    (0x7F, 0xFF) excluded."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0xE4]))
+    c = rng.integers(0, 254, (m, k), dtype=np.uint16)
+    c = c + (c >= 0x7F) + (c >= 0xFE)  # skip 0x7F and 0xFF
+    return c.astype(np.uint8)

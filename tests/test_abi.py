@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ("sol_attn_pool", "sol_attn_forward", "attn_lse_merge", "sol_attn_row_stats",
               "sol_attn_row_stats_moment", "sol_attn_workspace_size", "sol_attn_error_string", "sol_attn_proxy_scores",
-              "sol_attn_block_mask"):
+              "sol_attn_block_mask", "fp8_quantize_rows", "fp8_gemm_rowscale"):
         assert n in names
 
 
@@ -83,6 +83,12 @@ def test_other_entry_points_argument_errors(lib):
     assert rsm(FAKE, FAKE, FAKE, FAKE, 64, 64, 1, 128, 64, N, need, N) == -1      # no workspace
     assert rsm(FAKE, FAKE, FAKE, FAKE, 64, 64, 1, 128, 64, FAKE, need - 1, N) == -1  # too small
     assert rsm(FAKE, FAKE, FAKE, FAKE, 64, 64, 1, 96, 64, FAKE, need, N) == -2
+    assert lib.fp8_quantize_rows(N, FAKE, FAKE, ctypes.c_int64(4), 128, N) == -1
+    assert lib.fp8_quantize_rows(FAKE, FAKE, FAKE, ctypes.c_int64(4), 12, N) == -2  # K % 8
+    assert lib.fp8_gemm_rowscale(FAKE, FAKE, FAKE, FAKE, N, 4, 128, 128, N) == -1
+    assert lib.fp8_gemm_rowscale(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 128, 192, N) == -2  # K % 128
+    assert lib.fp8_gemm_rowscale(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 96, 128, N) == -2   # N % 128
+    assert lib.fp8_gemm_rowscale(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 128, 128, N) == -1
     assert lib.attn_lse_merge(FAKE, FAKE, FAKE, FAKE, FAKE, N, 64, 1, 128, N) == -1
     assert lib.attn_lse_merge(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 128, N) == -1
     assert lib.sol_attn_proxy_scores(FAKE, FAKE, FAKE, 60, 10, 64, 64, 1, 128, 64, N) == -1
