@@ -76,21 +76,23 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(Fp8QuantArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// GEMM.  Workgroup: 4 waves on a 256 (tokens) x 256 (channels) output tile;
-// wave (wm, wn) owns 128 x 128 as 4 x 4 MFMA tiles computed transposed
-// (D = W A^T: lane l holds token l % 32 and, per tile, channels in groups of
-// four consecutive ones, so each store writes 8 contiguous bytes).
-// K streams through a four-stage LDS ring in slices of 64 bytes per row
-// (16 KiB of tokens + 16 KiB of weights per stage), filled by direct
-// global->LDS loads three slices ahead.  A row's four 16-byte chunks sit at
-// chunk c ^ ((row / 4) % 4), so the 16 lanes of each read phase hit 16
+// GEMM.  Workgroup: 8 waves (two per SIMD) on a 256 (tokens) x 256 (channels)
+// output tile; wave (wm, wn) owns 128 tokens x 64 channels as 4 x 2 MFMA tiles
+// computed transposed (D = W A^T: lane l holds token l % 32 and, per tile,
+// channels in groups of four consecutive ones, so each store writes 8
+// contiguous bytes).  K streams through a five-stage LDS ring in slices of 64
+// bytes per row (16 KiB of tokens + 16 KiB of weights per stage), filled by
+// direct global->LDS loads four slices ahead; while one wave of a SIMD waits
+// for its operands the other issues products.  A row's four 16-byte chunks
+// sit at chunk c ^ ((row / 4) % 4), so the 16 lanes of each read phase hit 16
 // distinct bank groups.
 // ---------------------------------------------------------------------------
 constexpr int kGT = 256;              // tile edge (tokens and channels)
 constexpr int kGK = 64;               // K bytes per stage
-constexpr int kGStages = 4;
+constexpr int kGStages = 5;
 constexpr int kGStageBytes = kGT * kGK;  // per operand
-constexpr int kGDmaPerStage = 8;         // per wave: 4 token + 4 weight instructions
+constexpr int kGWaves = 8;
+constexpr int kGDmaPerStage = 4;         // per wave: 2 token + 2 weight instructions
 
 __device__ __forceinline__ int g_chunk(int row, int c) { return c ^ ((row >> 2) & 3); }
 
@@ -107,7 +109,7 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(Fp8GemmArgs a) {
+__global__ __launch_bounds__(512, 1) void fp8_gemm_kernel(Fp8GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[kGStages][kGStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds_w[kGStages][kGStageBytes];
 
@@ -125,13 +127,13 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(Fp8GemmArgs a) {
   const int m0 = tm * kGT, n0 = tn * kGT;
   const int K = a.K;
 
-  // direct loads: instruction i of this wave fills rows 16 (4 wave + i) .. +15
+  // direct loads: instruction i of this wave fills rows 16 (2 wave + i) .. +15
   // of a stage; lane l lands in row + l / 4, chunk slot l % 4
-  const uint8_t* abase[4];
-  const uint8_t* wbase[4];
+  const uint8_t* abase[2];
+  const uint8_t* wbase[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (wave * 4 + i) * 16 + (lane >> 2);
+  for (int i = 0; i < 2; ++i) {
+    const int r = (wave * 2 + i) * 16 + (lane >> 2);
     const int c = g_chunk(r, lane & 3);
     // rows past the end re-read the last row (finite data, never stored)
     const int ra = min(m0 + r, a.M - 1), rw = min(n0 + r, a.N - 1);
@@ -141,8 +143,8 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(Fp8GemmArgs a) {
   auto dma_stage = [&](int ks, int st) __attribute__((always_inline)) {
     const int64_t k0 = (int64_t)ks * kGK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r0 = (wave * 4 + i) * 16;
+    for (int i = 0; i < 2; ++i) {
+      const int r0 = (wave * 2 + i) * 16;
       g_dma16(abase[i] + k0, lds_addr(&lds_a[st][r0 * kGK]));
       g_dma16(wbase[i] + k0, lds_addr(&lds_w[st][r0 * kGK]));
     }
@@ -155,68 +157,85 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_kernel(Fp8GemmArgs a) {
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
+  // Every step issues one slice of loads (past the last slice it re-loads the
+  // last slice into the stage just freed, which is never read again), so the
+  // loads in flight are the same at every wait and each wait is one fixed
+  // instruction.
   const int nk = K / kGK;
+  constexpr int kYoung = (kGStages - 2) * kGDmaPerStage;  // loads of younger slices in flight
+  constexpr int kWaitSlice = (kYoung & 15) | ((kYoung >> 4) << 14) | 0x0F70;
 #pragma unroll
-  for (int s = 0; s < kGStages - 1; ++s)
-    if (s < nk) dma_stage(s, s);
-
-  for (int ks = 0; ks < nk; ++ks) {
-    // this wave's loads of slice ks have landed once at most the loads of the
-    // younger slices already issued are outstanding
-    const int younger = min(kGStages - 2, nk - 1 - ks);
-    if (younger >= 2)
-      __builtin_amdgcn_s_waitcnt((2 * kGDmaPerStage & 15) | (((2 * kGDmaPerStage) >> 4) << 14) | 0x0F70);
-    else if (younger == 1)
-      __builtin_amdgcn_s_waitcnt((kGDmaPerStage & 15) | ((kGDmaPerStage >> 4) << 14) | 0x0F70);
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    __builtin_amdgcn_s_barrier();
+  for (int s = 0; s < kGStages - 1; ++s) dma_stage(min(s, nk - 1), s);
+  for (int s = 0; s < nk; ++s) {
+    // this wave's loads of slice s landed (younger slices may be in flight)
+    __builtin_amdgcn_s_waitcnt(kWaitSlice);
+    __builtin_amdgcn_s_barrier();  // every wave: slice s landed, slice s - 1's stage read
     asm volatile("" ::: "memory");
-    if (ks + kGStages - 1 < nk) dma_stage(ks + kGStages - 1, (ks + kGStages - 1) % kGStages);
-    const int st = ks % kGStages;
-    const uint8_t* sa_ = lds_a[st];
-    const uint8_t* sw_ = lds_w[st];
-    i32x8 bt[4];
+    dma_stage(min(s + kGStages - 1, nk - 1), (s + kGStages - 1) % kGStages);
+    const int st = s % kGStages;
+    i32x8 am[4], wf[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) bt[mt] = frag(sa_, wm * 128 + mt * 32 + r32);
+    for (int mt = 0; mt < 4; ++mt) am[mt] = frag(lds_a[st], wm * 128 + mt * 32 + r32);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const i32x8 at = frag(sw_, wn * 128 + nt * 32 + r32);
+    for (int nt = 0; nt < 2; ++nt) wf[nt] = frag(lds_w[st], wn * 64 + nt * 32 + r32);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma_fp8(at, bt[mt], acc[mt][nt]);
-    }
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma_fp8(wf[nt], am[mt], acc[mt][nt]);
   }
   __builtin_amdgcn_s_waitcnt(0);
 
-  // epilogue: y[m][n] = acc * sa[m] * sw[n], bf16; lane holds token m and, per
-  // tile, channels n0 + 32 nt + 8 b + 4 g + (0..3) for b = 0..3
+  // epilogue: y[m][n] = acc * sa[m] * sw[n] in bf16, staged through LDS so that
+  // every store writes whole 128-byte rows.  Each wave owns 16 KiB of the
+  // (now idle) ring: its 128 x 64 tile, row-major, 16-byte chunk c of row r at
+  // c ^ (r % 8).  Lane l holds token row 32 mt + l % 32 and, per tile, the
+  // channels 32 nt + 8 b + 4 g + (0..3).
+  __builtin_amdgcn_s_barrier();  // every wave has read its last operands
+  asm volatile("" ::: "memory");
+  constexpr int kWaveTileBytes = 128 * 64 * 2;  // 128 tokens x 64 channels of bf16
+  uint8_t* stage = (wave < 4 ? &lds_a[0][0] : &lds_w[0][0]) + (wave & 3) * kWaveTileBytes;
+  float swr[2][4][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int n = min(n0 + wn * 64 + nt * 32 + 8 * b + 4 * g, a.N - 4);
+      const f32x4v v = gload<f32x4v>(a.sw + n);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) swr[nt][b][e] = v[e];
+    }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    const int m = m0 + wm * 128 + mt * 32 + r32;
-    if (m >= a.M) continue;
-    const float sm = a.sa[m];
-    uint16_t* yrow = a.y + (int64_t)m * a.N;
+    const int r = mt * 32 + r32;
+    const float sm = a.sa[min(m0 + wm * 128 + r, a.M - 1)];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int nb = n0 + wn * 128 + nt * 32;
-      if (nb >= a.N) continue;
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int n = nb + 8 * b + 4 * g;
-        const f32x4v swv = gload<f32x4v>(a.sw + n);
         u32x2 pk;
-        pk[0] = (uint32_t)f32_to_bf16_bits(acc[mt][nt][4 * b] * sm * swv[0]) |
-                ((uint32_t)f32_to_bf16_bits(acc[mt][nt][4 * b + 1] * sm * swv[1]) << 16);
-        pk[1] = (uint32_t)f32_to_bf16_bits(acc[mt][nt][4 * b + 2] * sm * swv[2]) |
-                ((uint32_t)f32_to_bf16_bits(acc[mt][nt][4 * b + 3] * sm * swv[3]) << 16);
-        *reinterpret_cast<u32x2*>(yrow + n) = pk;
+        pk[0] = (uint32_t)f32_to_bf16_bits(acc[mt][nt][4 * b] * sm * swr[nt][b][0]) |
+                ((uint32_t)f32_to_bf16_bits(acc[mt][nt][4 * b + 1] * sm * swr[nt][b][1]) << 16);
+        pk[1] = (uint32_t)f32_to_bf16_bits(acc[mt][nt][4 * b + 2] * sm * swr[nt][b][2]) |
+                ((uint32_t)f32_to_bf16_bits(acc[mt][nt][4 * b + 3] * sm * swr[nt][b][3]) << 16);
+        const int c = nt * 4 + b;  // 16-byte chunk of the 128-byte row; half g
+        *reinterpret_cast<u32x2*>(stage + r * 128 + ((c ^ (r & 7)) << 4) + g * 8) = pk;
       }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes done (wave-private region)
+  const int nw = n0 + wn * 64;
+  if (nw < a.N) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = i * 8 + (lane >> 3), pc = lane & 7;
+      const int m = m0 + wm * 128 + r;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * 128 + (pc << 4));
+      if (m < a.M) *reinterpret_cast<u32x4*>(a.y + (int64_t)m * a.N + nw + ((pc ^ (r & 7)) << 3)) = v;
     }
   }
 }
@@ -232,7 +251,7 @@ hipError_t launch_fp8_gemm(const Fp8GemmArgs& a0, hipStream_t s) {
   a.tiles_m = (a.M + kGT - 1) / kGT;
   a.tiles_n = (a.N + kGT - 1) / kGT;
   a.grid = (a.tiles_m * a.tiles_n + 7) & ~7;
-  fp8_gemm_kernel<<<a.grid, 256, 0, s>>>(a);
+  fp8_gemm_kernel<<<a.grid, kGWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
