@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA (twice the bf16 rate)
 PEAK_HBM_GBS = 8000.0
 METRIC = "ms/call + dense-equivalent TFLOP/s (% bf16 MFMA peak), 4K Stage-2 sparse attention"
 KERNEL_SOURCES = ["block_sparse_attention_06_amd/csrc/forward.hip",
@@ -99,6 +100,41 @@ def cpu_baseline(Q, K, V, B, beta, budget_s):
                   f"beta={beta}, fp64 numpy, {el:.1f} s wall",
         "ms_per_call_extrapolated": full_s * 1e3,
     }
+
+
+def fp8_projection(sa, torch, tokens, hidden, dev, stream, reps=5):
+    """FP8 projection around attention at the 4K token count: per-row E4M3
+    quantisation of bf16 activations [tokens, hidden], then the GEMM against
+    E4M3 weights [hidden, hidden] with per-channel scales (synthetic N(0, 1)
+    activations and N(0, 1/hidden) weights)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    x = torch.randn((tokens, hidden), generator=gen, device=dev).to(torch.bfloat16)
+    wt = (torch.randn((hidden, hidden), generator=gen, device=dev) * hidden ** -0.5).to(torch.bfloat16)
+    wq, wsc = sa.fp8_quantize_rows(wt)
+    aq = torch.empty((tokens, hidden), dtype=torch.uint8, device=dev)
+    asc = torch.empty((tokens,), dtype=torch.float32, device=dev)
+    y = torch.empty((tokens, hidden), dtype=torch.bfloat16, device=dev)
+    sa.fp8_quantize_rows(x, q=aq, scale=asc)
+    sa.fp8_gemm_rowscale(aq, asc, wq, wsc, out=y)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        sa.fp8_quantize_rows(x, q=aq, scale=asc)
+    ev[1].record(stream)
+    for _ in range(reps):
+        sa.fp8_gemm_rowscale(aq, asc, wq, wsc, out=y)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    q_ms = ev[0].elapsed_time(ev[1]) / reps
+    g_ms = ev[1].elapsed_time(ev[2]) / reps
+    flops = 2.0 * tokens * hidden * hidden
+    q_bytes = tokens * hidden * (2 + 1) + tokens * 4  # bf16 read once, codes + scales written
+    return {"tokens": tokens, "in_features": hidden, "out_features": hidden,
+            "quantize_ms": q_ms, "quantize_gbs": q_bytes / q_ms / 1e6,
+            "gemm_ms": g_ms, "gemm_tflops": flops / g_ms / 1e9,
+            "pct_fp8_peak": 100 * flops / g_ms / 1e9 / PEAK_FP8_TFLOPS}
 
 
 def main():
@@ -265,6 +301,7 @@ def main():
         ms = es[0].elapsed_time(es[1]) / 2
         extras["4k_dense"] = {"ms_per_call": ms, "tflops": dense_flops / ms / 1e9,
                               "pct_bf16_peak": 100 * dense_flops / ms / 1e9 / PEAK_BF16_TFLOPS}
+        extras["fp8_projection_4k"] = fp8_projection(sa, torch, N, H * d, q.device, stream)
 
     cpu = None
     if not args.no_cpu:

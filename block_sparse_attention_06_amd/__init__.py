@@ -265,14 +265,22 @@ def sol_attn_block_mask(q: torch.Tensor, kbar: torch.Tensor, mu: torch.Tensor,
     return mask, counts
 
 
-def fp8_quantize_rows(x: torch.Tensor, stream=None):
+def fp8_quantize_rows(x: torch.Tensor, q: Optional[torch.Tensor] = None,
+                      scale: Optional[torch.Tensor] = None, stream=None):
     """Per-row E4M3 quantisation of a bf16 ``[M, K]`` matrix: returns
-    ``(codes [M, K] uint8, scale [M] fp32)`` with ``x ~ scale[:, None] * dec(codes)``."""
+    ``(codes [M, K] uint8, scale [M] fp32)`` with ``x ~ scale[:, None] * dec(codes)``;
+    pass ``q`` and ``scale`` to write into existing tensors."""
     lib = load_library()
     _want(x, "x", torch.bfloat16, 2)
     M, K = x.shape
-    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-    scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _want(q, "q", torch.uint8, 2)
+    _want(scale, "scale", torch.float32, 1)
+    if tuple(q.shape) != (M, K) or scale.shape[0] != M:
+        raise ValueError("fp8_quantize_rows: output shape mismatch")
     _check("fp8_quantize_rows", lib.fp8_quantize_rows(_ptr(x), _ptr(q), _ptr(scale), M, K,
                                                       _stream(stream)))
     return q, scale

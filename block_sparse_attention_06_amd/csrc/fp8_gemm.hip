@@ -28,6 +28,8 @@ constexpr float kE4m3Max = 448.f;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
+}  // namespace
+
 // ---------------------------------------------------------------------------
 // Row quantisation.  One wave per row, 8 bf16 (16 bytes) per lane per step:
 // pass 1 finds the row's absolute maximum, pass 2 (reading the row again, now
@@ -74,6 +76,8 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(Fp8QuantArgs a) {
     *reinterpret_cast<u32x2*>(q + k) = out;
   }
 }
+
+namespace {
 
 // ---------------------------------------------------------------------------
 // GEMM.  Workgroup: 8 waves (two per SIMD) on a 256 (tokens) x 256 (channels)

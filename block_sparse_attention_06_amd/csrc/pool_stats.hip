@@ -168,13 +168,17 @@ hipError_t launch_stats(const StatsArgs& a, hipStream_t s) {
 // Row statistics in moment form.  p_ij - mu_i = s q_i . (kbar_j - mbar) is
 // linear in q_i, so over the blocks
 //   mu_i = s q_i . mbar,   sigma_i^2 = s^2 q_i^T C q_i,
-// with mbar the mean of the pooled keys and C their covariance (population,
-// centred, so no cancellation).  Same quantities as stats_kernel up to
+// with mbar the mean of the pooled keys and C their population covariance.
+// Same quantities as stats_kernel up to
 // rounding, at 2 d^2 instead of 2 d nb multiply-adds per row.
 //
-// moments_kernel: one workgroup per (16 rows of C, head).  The mean is summed
-// by all 256 threads (two per dimension), then 32 centred pooled keys at a
-// time are staged in LDS and each thread accumulates 8 entries of C in fp32.
+// moments_kernel: one workgroup per (16 rows of C, head), one pass over the
+// pooled keys.  32 keys at a time are staged in LDS, shifted by the head's
+// first pooled key (so the second moments carry no large common offset: the
+// shift-then-correct form keeps the cancellation to the keys' own spread),
+// while the next 32 are already being loaded; each thread accumulates 8
+// entries of the shifted second moment plus the shifted sums of its row and
+// columns, all in fp32.  C = S2 / nb - (S1_r / nb)(S1_c / nb); mbar = k0 + S1 / nb.
 // C is written as bf16 hi + lo parts (~16 significant bits), rows permuted
 // (see c_row_pos) so that stats_moment_kernel's accumulator elements line up
 // with its query fragment.
@@ -191,51 +195,66 @@ __device__ __forceinline__ int c_row_pos(int off) {
 
 __global__ __launch_bounds__(256) void moments_kernel(MomentArgs a) {
   __shared__ float kc[kChunk][kHeadDim + 4];
-  __shared__ float part[2][kHeadDim];
+  __shared__ float k0s[kHeadDim];
   const int rb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const float* kb = a.kbar + (int64_t)h * a.nb * kHeadDim;
-  {
-    const int dim = tid & (kHeadDim - 1), par = tid >> 7;
-    float acc = 0.f;
-    for (int j = par; j < a.nb; j += 2) acc += kb[(int64_t)j * kHeadDim + dim];
-    part[par][dim] = acc;
-  }
-  __syncthreads();
-  const float inv_nb = 1.f / (float)a.nb;
+  if (tid < kHeadDim) k0s[tid] = kb[tid];
+  constexpr int kPer = kChunk * kHeadDim / 256;  // staged values per thread
+  float nxt[kPer];
+  auto load = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = tid + 256 * i, j = j0 + (e >> 7);
+      nxt[i] = j < a.nb ? kb[(int64_t)j * kHeadDim + (e & (kHeadDim - 1))] : 0.f;
+    }
+  };
+  load(0);
   const int r = rb * 16 + (tid >> 4), c0 = (tid & 15) * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float sc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float sr = 0.f;
   for (int j0 = 0; j0 < a.nb; j0 += kChunk) {
-    __syncthreads();  // the previous chunk has been consumed
-    for (int e = tid; e < kChunk * kHeadDim; e += 256) {
-      const int rr = e >> 7, cc = e & (kHeadDim - 1), j = j0 + rr;
-      const float mean = (part[0][cc] + part[1][cc]) * inv_nb;
-      kc[rr][cc] = j < a.nb ? kb[(int64_t)j * kHeadDim + cc] - mean : 0.f;
+    __syncthreads();  // the previous chunk has been consumed (and k0s is visible)
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = tid + 256 * i, j = j0 + (e >> 7), cc = e & (kHeadDim - 1);
+      kc[e >> 7][cc] = j < a.nb ? nxt[i] - k0s[cc] : 0.f;
     }
     __syncthreads();
+    if (j0 + kChunk < a.nb) load(j0 + kChunk);
     const int nj = min(kChunk, a.nb - j0);
     for (int jj = 0; jj < nj; ++jj) {
       const float x = kc[jj][r];
       const f32x4 y0 = *reinterpret_cast<const f32x4*>(&kc[jj][c0]);
       const f32x4 y1 = *reinterpret_cast<const f32x4*>(&kc[jj][c0 + 4]);
+      sr += x;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         acc[k] = __builtin_fmaf(x, y0[k], acc[k]);
         acc[k + 4] = __builtin_fmaf(x, y1[k], acc[k + 4]);
+        sc[k] += y0[k];
+        sc[k + 4] += y1[k];
       }
     }
   }
+  const float inv_nb = 1.f / (float)a.nb;
+  const float mr = sr * inv_nb;
   bf16x8 hi, lo;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     __bf16 hh, ll;
-    split_bf16(acc[k] * inv_nb, hh, ll);
+    split_bf16(__builtin_fmaf(-mr, sc[k] * inv_nb, acc[k] * inv_nb), hh, ll);
     hi[k] = hh;
     lo[k] = ll;
   }
   const int64_t pos = ((int64_t)h * kHeadDim + (r & ~31) + c_row_pos(r & 31)) * kHeadDim + c0;
   *reinterpret_cast<bf16x8*>(a.chi + pos) = hi;
   *reinterpret_cast<bf16x8*>(a.clo + pos) = lo;
-  if (rb == 0 && tid < kHeadDim) a.mbar[(int64_t)h * kHeadDim + tid] = (part[0][tid] + part[1][tid]) * inv_nb;
+  if (rb == 0 && (tid >> 4) == 0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      a.mbar[(int64_t)h * kHeadDim + c0 + k] = k0s[c0 + k] + sc[k] * inv_nb;
+  }
 }
 
 hipError_t launch_moments(const MomentArgs& a, hipStream_t s) {
@@ -243,19 +262,21 @@ hipError_t launch_moments(const MomentArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// stats_moment_kernel: one wave per 32 query rows, four per workgroup.  C (hi
-// and lo, 64 KiB) is staged in LDS (16-byte chunk c of row R at c ^ (R % 16));
-// Y^T = C Q^T runs on MFMA as 4 row tiles x 8 k-steps x (hi, lo), then each
-// lane dots its 64 accumulator elements with the matching query values, which
-// it already holds as MFMA operands, and adds the partner lane's half.
+// stats_moment_kernel: one wave per 32 query rows, four per 128-row tile, and
+// kMomentTiles consecutive tiles per workgroup, so that C (hi and lo, 64 KiB)
+// is staged in LDS once per 1024 rows (16-byte chunk c of row R at
+// c ^ (R % 16)).  Y^T = C Q^T runs on MFMA as 4 row tiles x 8 k-steps x (hi,
+// lo); each lane dots its 64 accumulator elements with the matching query
+// values, which it already holds as MFMA operands, and adds the partner lane's
+// half.  The next tile's query fragment is loaded while this one's products run.
+constexpr int kMomentTiles = 8;
+
 __global__ __launch_bounds__(256) void stats_moment_kernel(StatsMomentArgs a) {
   __shared__ __attribute__((aligned(16))) u16 chs[kHeadDim * kHeadDim];
   __shared__ __attribute__((aligned(16))) u16 cls[kHeadDim * kHeadDim];
   __shared__ float mb[kHeadDim];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
   const int h = blockIdx.y;
-  const int row = blockIdx.x * kQTile + wave * 32 + (lane & 31);
-  const bool valid = row < a.N;
   const u16* ch = a.chi + (int64_t)h * kHeadDim * kHeadDim;
   const u16* cl = a.clo + (int64_t)h * kHeadDim * kHeadDim;
   for (int e = tid; e < kHeadDim * 16; e += 256) {
@@ -267,45 +288,56 @@ __global__ __launch_bounds__(256) void stats_moment_kernel(StatsMomentArgs a) {
     *reinterpret_cast<u32x4*>(&cls[off]) = xl;
   }
   if (tid < kHeadDim) mb[tid] = a.mbar[(int64_t)h * kHeadDim + tid];
+  const u16* qh = a.q + (int64_t)h * a.N * kHeadDim;
+  const int row0 = blockIdx.x * kMomentTiles * kQTile + wave * 32 + (lane & 31);
   QFrag qf;
-  load_qfrag(qf, a.q + (int64_t)h * a.N * kHeadDim, row, valid, g);
+  load_qfrag(qf, qh, row0, row0 < a.N, g);
   __syncthreads();
   const int r = lane & 31;
-  f32x16 y[4];
+  for (int t = 0; t < kMomentTiles; ++t) {
+    const int row = row0 + t * kQTile;
+    if (row - (lane & 31) >= a.N) break;  // wave-uniform: the wave's first row is past the end
+    const bool valid = row < a.N;
+    QFrag qn;
+    const int rown = row + kQTile;
+    if (t + 1 < kMomentTiles) load_qfrag(qn, qh, rown, rown < a.N, g);
+    f32x16 y[4];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    y[ct] = f32x16{};
-    const int R = ct * 32 + r;
+    for (int ct = 0; ct < 4; ++ct) {
+      y[ct] = f32x16{};
+      const int R = ct * 32 + r;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int off = R * kHeadDim + (((ks * 2 + g) ^ (R & 15)) << 3);
-      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(&chs[off]);
-      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(&cls[off]);
-      y[ct] = mfma32(hi, qf.k[ks], y[ct]);
-      y[ct] = mfma32(lo, qf.k[ks], y[ct]);
+      for (int ks = 0; ks < 8; ++ks) {
+        const int off = R * kHeadDim + (((ks * 2 + g) ^ (R & 15)) << 3);
+        const bf16x8 hi = *reinterpret_cast<const bf16x8*>(&chs[off]);
+        const bf16x8 lo = *reinterpret_cast<const bf16x8*>(&cls[off]);
+        y[ct] = mfma32(hi, qf.k[ks], y[ct]);
+        y[ct] = mfma32(lo, qf.k[ks], y[ct]);
+      }
     }
-  }
-  float s1 = 0.f, s2 = 0.f;
+    float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
+    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      s2 = __builtin_fmaf(y[ct][e], (float)qf.k[2 * ct + (e >> 3)][e & 7], s2);
+      for (int e = 0; e < 16; ++e)
+        s2 = __builtin_fmaf(y[ct][e], (float)qf.k[2 * ct + (e >> 3)][e & 7], s2);
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) s1 = __builtin_fmaf((float)qf.k[ks][k], mb[16 * ks + 8 * g + k], s1);
-  s1 += __shfl_xor(s1, 32);
-  s2 += __shfl_xor(s2, 32);
-  if (g == 0 && valid) {
-    const float scale = 0.08838834764831845f;  // 1/sqrt(128)
-    a.mu[(int64_t)h * a.N + row] = s1 * scale;
-    a.sigma[(int64_t)h * a.N + row] = sqrtf(fmaxf(s2, 0.f)) * scale;
+      for (int k = 0; k < 8; ++k) s1 = __builtin_fmaf((float)qf.k[ks][k], mb[16 * ks + 8 * g + k], s1);
+    s1 += __shfl_xor(s1, 32);
+    s2 += __shfl_xor(s2, 32);
+    if (g == 0 && valid) {
+      const float scale = 0.08838834764831845f;  // 1/sqrt(128)
+      a.mu[(int64_t)h * a.N + row] = s1 * scale;
+      a.sigma[(int64_t)h * a.N + row] = sqrtf(fmaxf(s2, 0.f)) * scale;
+    }
+    if (t + 1 < kMomentTiles) qf = qn;
   }
 }
 
 hipError_t launch_stats_moment(const StatsMomentArgs& a, hipStream_t s) {
-  dim3 grid((a.N + kQTile - 1) / kQTile, a.H);
+  dim3 grid((a.N + kMomentTiles * kQTile - 1) / (kMomentTiles * kQTile), a.H);
   stats_moment_kernel<<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
