@@ -32,49 +32,75 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // Row quantisation.  One wave per row, 8 bf16 (16 bytes) per lane per step:
-// pass 1 finds the row's absolute maximum, pass 2 (reading the row again, now
-// from cache) scales, clamps to +-448 (a scaled maximum may land one float32
-// ulp above it) and converts pairs with v_cvt_pk_fp8_f32 (round to nearest
-// even).
+// pass 1 finds the row's absolute maximum, pass 2 scales, clamps to +-448 (a
+// scaled maximum may land one float32 ulp above it) and converts pairs with
+// v_cvt_pk_fp8_f32 (round to nearest even).  Rows of up to kQuantKeep * 512
+// elements stay in registers between the passes, so the row is read once;
+// longer rows are read again (from cache) in pass 2.
 // ---------------------------------------------------------------------------
+constexpr int kQuantKeep = 8;
+
+__device__ __forceinline__ u32x2 quant8(u32x4 v, float inv) {
+  u32x2 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float f[4];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      f[2 * e] = __uint_as_float(v[2 * h + e] << 16) * inv;
+      f[2 * e + 1] = __uint_as_float(v[2 * h + e] & 0xFFFF0000u) * inv;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = fminf(fmaxf(f[e], -kE4m3Max), kE4m3Max);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w, true);
+    out[h] = (uint32_t)w;
+  }
+  return out;
+}
+
+__device__ __forceinline__ float absmax8(u32x4 v, float m) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    m = fmaxf(m, fabsf(__uint_as_float(v[e] << 16)));
+    m = fmaxf(m, fabsf(__uint_as_float(v[e] & 0xFFFF0000u)));
+  }
+  return m;
+}
+
 __global__ __launch_bounds__(256) void quantize_rows_kernel(Fp8QuantArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.M) return;
   const u16* x = a.x + row * a.K;
+  uint8_t* q = a.q + row * a.K;
   float amax = 0.f;
-  for (int k = lane * 8; k < a.K; k += 512) {
-    const u32x4 v = gload<u32x4>(x + k);
+  if (a.K <= kQuantKeep * 512) {
+    u32x4 keep[kQuantKeep];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      amax = fmaxf(amax, fabsf(__uint_as_float(v[e] << 16)));
-      amax = fmaxf(amax, fabsf(__uint_as_float(v[e] & 0xFFFF0000u)));
+    for (int i = 0; i < kQuantKeep; ++i) {
+      const int k = lane * 8 + i * 512;
+      keep[i] = k < a.K ? gload<u32x4>(x + k) : u32x4{0u, 0u, 0u, 0u};
+      amax = absmax8(keep[i], amax);
     }
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) amax = fmaxf(amax, __shfl_xor(amax, sh));
+    const float inv = amax > 0.f ? kE4m3Max / amax : 0.f;
+    if (lane == 0) a.scale[row] = amax / kE4m3Max;
+#pragma unroll
+    for (int i = 0; i < kQuantKeep; ++i) {
+      const int k = lane * 8 + i * 512;
+      if (k < a.K) *reinterpret_cast<u32x2*>(q + k) = quant8(keep[i], inv);
+    }
+    return;
   }
+  for (int k = lane * 8; k < a.K; k += 512) amax = absmax8(gload<u32x4>(x + k), amax);
 #pragma unroll
   for (int sh = 1; sh < 64; sh <<= 1) amax = fmaxf(amax, __shfl_xor(amax, sh));
   const float inv = amax > 0.f ? kE4m3Max / amax : 0.f;
   if (lane == 0) a.scale[row] = amax / kE4m3Max;
-  uint8_t* q = a.q + row * a.K;
-  for (int k = lane * 8; k < a.K; k += 512) {
-    const u32x4 v = gload<u32x4>(x + k);
-    u32x2 out;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float f[4];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        f[2 * e] = __uint_as_float(v[2 * h + e] << 16) * inv;
-        f[2 * e + 1] = __uint_as_float(v[2 * h + e] & 0xFFFF0000u) * inv;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) f[e] = fminf(fmaxf(f[e], -kE4m3Max), kE4m3Max);
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w, true);
-      out[h] = (uint32_t)w;
-    }
-    *reinterpret_cast<u32x2*>(q + k) = out;
-  }
+  for (int k = lane * 8; k < a.K; k += 512)
+    *reinterpret_cast<u32x2*>(q + k) = quant8(gload<u32x4>(x + k), inv);
 }
 
 namespace {

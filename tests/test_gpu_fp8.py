@@ -29,7 +29,7 @@ def _bf16_to_f64(t):
         np.float32).astype(np.float64)
 
 
-@pytest.mark.parametrize("M,K", [(1, 128), (37, 4096), (1000, 520), (5, 8)])
+@pytest.mark.parametrize("M,K", [(1, 128), (37, 4096), (1000, 520), (5, 8), (9, 4104), (3, 8192)])
 def test_quantize_rows_bit_exact(M, K):
     x = activations(M, K, seed=M + K)
     x[0, :] = 0                                   # all-zero row
