@@ -250,7 +250,7 @@ int sol_attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, ui
   if (use_pp) {
     FwdArgs fp = f;
     fp.total = (int)pp_wgs;
-    if (int r = hip_status(launch_forward_pp(fp, false, 128, s))) return r;
+    if (int r = hip_status(launch_forward_pp(fp, s))) return r;
   } else {
     if (int r = hip_status(launch_forward(f, sparse, sparse ? B : 128, s))) return r;
   }

@@ -1,11 +1,7 @@
-// Long-sequence forward kernel for gfx950: the same computation as fwd_kernel
-// (dense softmax attention, or thresholded block-sparse attention with the
-// first-order Taylor term), scheduled so that matrix and vector work overlap.
-//
-// Sol-Engine LTX25 page, "Stage 2 Optimization -- Core Technology: Sol-Attn":
-// routing folded into the online-softmax pass (pooled keys compared with each
-// row's threshold chunk by chunk, proxy map never stored); rejected blocks
-// enter through n_j e^{mu_i} (1 + p_ij - mu_i) on the pooled value.
+// Long-sequence dense forward kernel for gfx950: plain softmax attention (the
+// dense mode of the forward entry point, and its sparse mode with beta = -inf),
+// scheduled so that matrix and vector work overlap.  The sparse method runs in
+// fwd_kernel, whose independent 4-wave workgroups suit per-wave skipping.
 //
 // Schedule.  A workgroup is 8 waves on 256 query rows of one head: group 0
 // (waves 0-3) owns query rows 0-127, group 1 (waves 4-7) rows 128-255; each
@@ -55,11 +51,9 @@ __device__ __forceinline__ void pp_barrier() {
 
 }  // namespace
 
-template <bool SPARSE, int KB>
 __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) u16 lds_k[kPPStages][kPPStageElems];
   __shared__ __attribute__((aligned(16))) u16 lds_v[kPPStages][kPPStageElems];
-  __shared__ uint32_t wmask[2][8];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, r32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -79,24 +73,13 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
   const u16* kh = a.k + (int64_t)h * a.Nk * kHeadDim;
   const u16* vh = a.v + (int64_t)h * a.Nk * kHeadDim;
   const int Nk = a.Nk;
-  const int nb = a.nb;
   const float sl2 = 0.08838834764831845f * kLog2e;
 
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
   float l = 0.f;
-  float m;
-  float mu = 0.f, tau = __builtin_inff();
-  if constexpr (SPARSE) {
-    if (qvalid) {
-      mu = gload<float>(a.mu + (int64_t)h * a.N + row);
-      tau = make_tau(mu, gload<float>(a.sigma + (int64_t)h * a.N + row), a.beta);
-    }
-    m = mu * kLog2e;
-  } else {
-    m = -__builtin_inff();
-  }
+  float m = -__builtin_inff();
 
   // The query fragment and row statistics are the only loads the compiler
   // tracks; drain them here so that no wait it places later also waits for
@@ -136,100 +119,15 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
   bool stream_done = false;
   int u_next = 0;
   const int u_end = (Nk + kPPUnit - 1) / kPPUnit;
-  int c_next = 0, cA = 0, parity = 0;
-  uint32_t UA = 0, fullA = 0, wvA = 0;
-  int pend_left = 0, pend_key = 0;
-  bool pend_mine = false, pend_need = false;
-  const u16* khi = SPARSE ? a.khi + (int64_t)h * a.nb_pad * kHeadDim : nullptr;
-  const u16* klo = SPARSE ? a.klo + (int64_t)h * a.nb_pad * kHeadDim : nullptr;
-  const u16* vsum = SPARSE ? a.vsumT + (int64_t)h * kHeadDim * a.nb_pad : nullptr;
 
   auto gen = [&](int& key0, bool& mi, bool& ne) __attribute__((always_inline)) -> bool {
     if (stream_done) return false;
     bool have = false;
-    if constexpr (SPARSE) {
-      if (pend_left == 0) {
-        while (UA == 0 && c_next < nb) {
-          // route a chunk of 32 blocks: proxy scores, selection, Taylor part
-          if (o_rescale) {  // the Taylor terms below are relative to the current m
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) o[dt] *= o_scale;
-            o_scale = 1.f;
-            o_rescale = false;
-          }
-          const int c0 = c_next;
-          const f32x16 p = proxy_chunk_hl(qf, khi, klo, c0, lane);
-          const float f = fast_exp2(mu * kLog2e - m);
-          uint32_t sel_bits = 0;
-          bf16x8 whi[2], wlo[2];
-          float wden = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int off = acc_row(i, g);
-            const int blk = c0 + off;
-            const bool inr = qvalid && blk < nb;
-            const bool sel = inr && is_selected(p[i], tau);
-            sel_bits |= (uint32_t)sel << off;
-            const float wt = (inr && !sel) ? (1.f + p[i] - mu) * f : 0.f;
-            __bf16 wh, wl;
-            split_bf16(wt, wh, wl);
-            whi[i >> 3][i & 7] = wh;
-            wlo[i >> 3][i & 7] = wl;
-            const int nj = inr ? min(KB, Nk - blk * KB) : 0;
-            wden = __builtin_fmaf((float)nj, wt, wden);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-              const u32x4 va =
-                  gload<u32x4>(vsum + (int64_t)(dt * 32 + r32) * a.nb_pad + c0 + h2 * 16 + g * 8);
-              o[dt] = mfma32(as_bf16x8(va), whi[h2], o[dt]);
-              o[dt] = mfma32(as_bf16x8(va), wlo[h2], o[dt]);
-            }
-          }
-          l += wden;
-          fullA = sel_bits | pp_partner_u(sel_bits, g);
-          uint32_t w = fullA;
-#pragma unroll
-          for (int sh = 1; sh < 32; sh <<= 1) w |= __shfl_xor(w, sh);
-          wvA = w;
-          if (lane == 0) wmask[parity][wave] = w;
-          __builtin_amdgcn_s_waitcnt(kPPWaitLgkm0);
-          pp_barrier();
-          uint32_t un = 0;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) un |= wmask[parity][i];
-          UA = un;
-          cA = c0;
-          c_next += kChunk;
-          parity ^= 1;
-        }
-        if (UA) {
-          const int b = __builtin_ctz(UA);
-          UA &= UA - 1;
-          pend_key = (cA + b) * KB;
-          pend_left = KB / kPPUnit;
-          pend_mine = ((fullA >> b) & 1u) != 0;
-          pend_need = ((wvA >> b) & 1u) != 0;
-        }
-      }
-      if (pend_left > 0) {
-        have = true;
-        key0 = pend_key;
-        mi = pend_mine;
-        ne = pend_need;
-        pend_key += kPPUnit;
-        --pend_left;
-      }
-    } else {
-      if (u_next < u_end) {
-        have = true;
-        key0 = u_next * kPPUnit;
-        mi = ne = true;
-        ++u_next;
-      }
+    if (u_next < u_end) {
+      have = true;
+      key0 = u_next * kPPUnit;
+      mi = ne = true;
+      ++u_next;
     }
     stream_done = !have;
     return have;
@@ -409,10 +307,8 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
   if (a.lse && g == 0) a.lse[(int64_t)h * a.N + row] = m * kLn2 + logf(lt);
 }
 
-hipError_t launch_forward_pp(const FwdArgs& a, bool sparse, int B, hipStream_t s) {
-  (void)B;
-  if (sparse) return hipErrorInvalidValue;  // sparse attention runs the 4-wave kernel
-  fwd_pp_kernel<false, 128><<<a.total, 512, 0, s>>>(a);
+hipError_t launch_forward_pp(const FwdArgs& a, hipStream_t s) {
+  fwd_pp_kernel<<<a.total, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -127,7 +127,7 @@ hipError_t launch_stats_moment(const StatsMomentArgs& a, hipStream_t s);
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t s);
 hipError_t launch_forward(const FwdArgs& a, bool sparse, int B, hipStream_t s);
-hipError_t launch_forward_pp(const FwdArgs& a, bool sparse, int B, hipStream_t s);
+hipError_t launch_forward_pp(const FwdArgs& a, hipStream_t s);  // dense only
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_quantize_rows(const Fp8QuantArgs& a, hipStream_t s);
