@@ -36,6 +36,7 @@ __all__ = [
     "sol_attn_block_mask",
     "fp8_quantize_rows",
     "fp8_gemm_rowscale",
+    "na3d_forward",
 ]
 
 SOL_DENSE = 0
@@ -84,6 +85,7 @@ def load_library() -> ctypes.CDLL:
         "sol_attn_block_mask": (I, [P, P, P, P, F, I, I, I, I, I, I, I, P, P, P]),
         "fp8_quantize_rows": (I, [P, P, P, L, I, P]),
         "fp8_gemm_rowscale": (I, [P, P, P, P, P, I, I, I, P]),
+        "na3d_forward": (I, [P, P, P, P, P, I, I, I, I, I, I, I, I, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -305,3 +307,24 @@ def fp8_gemm_rowscale(a: torch.Tensor, sa: torch.Tensor, w: torch.Tensor, sw: to
     _check("fp8_gemm_rowscale", lib.fp8_gemm_rowscale(_ptr(a), _ptr(sa), _ptr(w), _ptr(sw),
                                                       _ptr(out), M, N, K, _stream(stream)))
     return out
+
+
+def na3d_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid, window,
+                 out: Optional[torch.Tensor] = None, want_lse: bool = True, stream=None):
+    """3D neighbourhood attention: ``q, k, v [H, T*Y*X, 128]`` bf16 on the grid
+    ``(T, Y, X)``, window ``(kt, ky, kx)`` (odd); returns ``(out, lse or None)``."""
+    lib = load_library()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _want(t, nm, torch.bfloat16, 3)
+    H, n, d = q.shape
+    T, Y, X = (int(x) for x in grid)
+    kt, ky, kx = (int(x) for x in window)
+    if n != T * Y * X or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("na3d_forward: shapes do not match the grid")
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((H, n), dtype=torch.float32, device=q.device) if want_lse else None
+    _check("na3d_forward", lib.na3d_forward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse) if lse is not None else None,
+        T, Y, X, H, d, kt, ky, kx, _stream(stream)))
+    return out, lse

@@ -182,6 +182,22 @@ int fp8_gemm_rowscale(const uint8_t* a, const float* sa, const uint8_t* w, const
   return hip_status(launch_fp8_gemm(g, (hipStream_t)stream));
 }
 
+int na3d_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                 float* lse, int T, int Y, int X, int H, int d, int kt, int ky, int kx,
+                 void* stream) {
+  if (!q || !k || !v || !out) return SOL_ERR_INVALID_ARG;
+  if (T <= 0 || Y <= 0 || X <= 0 || H <= 0) return SOL_ERR_INVALID_ARG;
+  if (d != 128) return SOL_ERR_UNSUPPORTED;
+  auto odd_fits = [](int w, int len) { return w >= 1 && (w & 1) && w <= len; };
+  if (!odd_fits(kt, T) || !odd_fits(ky, Y) || !odd_fits(kx, X)) return SOL_ERR_INVALID_ARG;
+  if (kx > 17) return SOL_ERR_UNSUPPORTED;
+  if ((long long)T * Y * X > (1LL << 31) / 128) return SOL_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return SOL_ERR_INVALID_ARG;
+  Na3dArgs a{q, k, v, out, lse, T, Y, X, H, kt, ky, kx};
+  return hip_status(launch_na3d(a, (hipStream_t)stream));
+}
+
 size_t sol_attn_workspace_size(int N, int Nk, int H, int d, int B, int mode) {
   if (Nk == 0) Nk = N;
   if (N <= 0 || Nk <= 0 || H <= 0 || d != 128) return 0;

@@ -63,6 +63,16 @@ struct Fp8GemmArgs {
   int tiles_m, tiles_n, grid;  // set by the launcher
 };
 
+struct Na3dArgs {
+  const uint16_t* q;  // [H, T*Y*X, 128] bf16, frame-major then row-major
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  float* lse;         // [H, T*Y*X] or null
+  int T, Y, X, H;
+  int kt, ky, kx;     // odd window sizes, kx <= 17
+};
+
 struct ProxyArgs {
   const uint16_t* q;
   const float* kbar;
@@ -132,5 +142,6 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_quantize_rows(const Fp8QuantArgs& a, hipStream_t s);
 hipError_t launch_fp8_gemm(const Fp8GemmArgs& a, hipStream_t s);
+hipError_t launch_na3d(const Na3dArgs& a, hipStream_t s);
 
 }  // namespace solattn

@@ -216,6 +216,23 @@ int fp8_quantize_rows(const uint16_t* x, uint8_t* q, float* scale, int64_t M, in
 int fp8_gemm_rowscale(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                       uint16_t* y, int M, int N, int K, void* stream);
 
+/*
+ * 3D neighbourhood attention over a video token grid (the diffusion video
+ * decoder's attention).
+ *   [DAI] "LTX-2.5 at 4K, in half the time" (doubleAI), section "Inside the
+ *   decoder"; the na3d backends named by the LTX-2 pipelines optimization guide.
+ * The query at (t, y, x) attends to the kt x ky x kx keys of the window centred
+ * on it and shifted inward at the borders (start clamp(p - k/2, 0, L - k) per
+ * axis), softmax with scale 1/sqrt(d).
+ * q, k, v  [H, T*Y*X, d] bf16 (read), tokens frame-major then row-major.
+ * out      [H, T*Y*X, d] bf16 (written).  lse [H, T*Y*X] fp32 (may be NULL).
+ * kt, ky, kx odd and at most T, Y, X (SOL_ERR_INVALID_ARG otherwise);
+ * d = 128 and kx <= 17 (SOL_ERR_UNSUPPORTED otherwise).  16-byte alignment.
+ */
+int na3d_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                 float* lse, int T, int Y, int X, int H, int d, int kt, int ky, int kx,
+                 void* stream);
+
 #if defined(__GNUC__)
 #pragma GCC visibility pop
 #endif

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ("sol_attn_pool", "sol_attn_forward", "attn_lse_merge", "sol_attn_row_stats",
               "sol_attn_row_stats_moment", "sol_attn_workspace_size", "sol_attn_error_string", "sol_attn_proxy_scores",
-              "sol_attn_block_mask", "fp8_quantize_rows", "fp8_gemm_rowscale"):
+              "sol_attn_block_mask", "fp8_quantize_rows", "fp8_gemm_rowscale", "na3d_forward"):
         assert n in names
 
 
@@ -83,6 +83,12 @@ def test_other_entry_points_argument_errors(lib):
     assert rsm(FAKE, FAKE, FAKE, FAKE, 64, 64, 1, 128, 64, N, need, N) == -1      # no workspace
     assert rsm(FAKE, FAKE, FAKE, FAKE, 64, 64, 1, 128, 64, FAKE, need - 1, N) == -1  # too small
     assert rsm(FAKE, FAKE, FAKE, FAKE, 64, 64, 1, 96, 64, FAKE, need, N) == -2
+    na = lib.na3d_forward
+    assert na(N, FAKE, FAKE, FAKE, N, 2, 8, 8, 1, 128, 1, 3, 3, N) == -1        # null q
+    assert na(FAKE, FAKE, FAKE, FAKE, N, 2, 8, 8, 1, 128, 2, 3, 3, N) == -1     # even window
+    assert na(FAKE, FAKE, FAKE, FAKE, N, 2, 8, 8, 1, 128, 3, 3, 3, N) == -1     # window > T
+    assert na(FAKE, FAKE, FAKE, FAKE, N, 2, 8, 40, 1, 128, 1, 3, 19, N) == -2   # kx > 17
+    assert na(FAKE, FAKE, FAKE, FAKE, N, 2, 8, 8, 1, 64, 1, 3, 3, N) == -2      # d != 128
     assert lib.fp8_quantize_rows(N, FAKE, FAKE, ctypes.c_int64(4), 128, N) == -1
     assert lib.fp8_quantize_rows(FAKE, FAKE, FAKE, ctypes.c_int64(4), 12, N) == -2  # K % 8
     assert lib.fp8_gemm_rowscale(FAKE, FAKE, FAKE, FAKE, N, 4, 128, 128, N) == -1
