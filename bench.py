@@ -137,6 +137,42 @@ def fp8_projection(sa, torch, tokens, hidden, dev, stream, reps=5):
             "pct_fp8_peak": 100 * flops / g_ms / 1e9 / PEAK_FP8_TFLOPS}
 
 
+def na3d_decoder_tile(sa, torch, dev, stream, reps=10):
+    """3D neighbourhood attention over one decoder tile of four latent frames
+    of the 4K grid (4 x 68 x 120 tokens), 16 heads of 128, window 3 x 7 x 7
+    (synthetic N(0, 1) bf16).  Algorithmic bytes: q, k, v read once, out and
+    lse written once; algorithmic flops 4 d per (query, window key)."""
+    T, Y, X, H, d = 4, 68, 120, 16, 128
+    kt, ky, kx = 3, 7, 7
+    n = T * Y * X
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    q, k, v = (torch.randn((H, n, d), generator=gen, device=dev).to(torch.bfloat16)
+               for _ in range(3))
+    out = torch.empty_like(q)
+    sa.na3d_forward(q, k, v, (T, Y, X), (kt, ky, kx), out=out)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        sa.na3d_forward(q, k, v, (T, Y, X), (kt, ky, kx), out=out)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    alg_bytes = H * n * (4 * d * 2 + 4)
+    alg_flops = 4.0 * d * kt * ky * kx * H * n
+    # keys multiplied on the matrix core: a wave of 32 queries (4 rows x 8
+    # columns of one frame) multiplies, in each of its kt key frames, the
+    # 3 + ky key rows of its patch in pairs of 16-column rows
+    exec_flops = 4.0 * d * kt * ((3 + ky + 1) // 2) * 32 * H * n
+    achieved = alg_bytes / ms / 1e6
+    return {"grid": [T, Y, X], "window": [kt, ky, kx], "heads": H, "head_dim": d,
+            "ms": ms, "alg_tflops": alg_flops / ms / 1e9,
+            "executed_mfma_tflops": exec_flops / ms / 1e9,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -302,6 +338,7 @@ def main():
         extras["4k_dense"] = {"ms_per_call": ms, "tflops": dense_flops / ms / 1e9,
                               "pct_bf16_peak": 100 * dense_flops / ms / 1e9 / PEAK_BF16_TFLOPS}
         extras["fp8_projection_4k"] = fp8_projection(sa, torch, N, H * d, q.device, stream)
+        extras["na3d_decoder_tile_4k"] = na3d_decoder_tile(sa, torch, q.device, stream)
 
     cpu = None
     if not args.no_cpu:

@@ -190,7 +190,7 @@ int na3d_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16
   if (d != 128) return SOL_ERR_UNSUPPORTED;
   auto odd_fits = [](int w, int len) { return w >= 1 && (w & 1) && w <= len; };
   if (!odd_fits(kt, T) || !odd_fits(ky, Y) || !odd_fits(kx, X)) return SOL_ERR_INVALID_ARG;
-  if (kx > 17) return SOL_ERR_UNSUPPORTED;
+  if (kx > 25) return SOL_ERR_UNSUPPORTED;
   if ((long long)T * Y * X > (1LL << 31) / 128) return SOL_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
     return SOL_ERR_INVALID_ARG;

@@ -70,7 +70,7 @@ struct Na3dArgs {
   uint16_t* out;
   float* lse;         // [H, T*Y*X] or null
   int T, Y, X, H;
-  int kt, ky, kx;     // odd window sizes, kx <= 17
+  int kt, ky, kx;     // odd window sizes, kx <= 25
 };
 
 struct ProxyArgs {

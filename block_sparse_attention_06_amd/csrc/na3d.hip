@@ -7,15 +7,18 @@
 // shifted inward at the grid's borders (start = clamp(p - k/2, 0, L - k) per
 // axis); plain softmax attention with scale 1/sqrt(d) inside the window.
 //
-// Workgroup: 4 waves on a brick of 1 frame x 8 rows x 16 columns of queries;
-// wave w owns rows 2w and 2w + 1 (32 queries, lane l % 32 = one query, in the
-// transposed "lane owns a row" MFMA formulation of the attention kernels).
-// The keys any query of the brick can see are kt frames x (8 + ky - 1) rows x
-// at most 16 + kx - 1 <= 32 columns; they stream through LDS as units of one
-// (frame, row) and 32 consecutive columns (K and V, 16 KiB), in a
-// three-stage ring filled by direct global->LDS loads two units ahead.  A wave
-// skips the products of units whose row no query of it can see; inside a
-// unit, keys outside a query's window get probability 0.
+// Workgroup: 4 waves on one patch of 4 rows x 8 columns of queries in four
+// consecutive frames; wave w owns the patch in frame 4 b + w (32 queries,
+// lane l % 32 = one query, in the transposed "lane owns a row" MFMA
+// formulation of the attention kernels).  All four waves see the same rows
+// and columns of keys (at most 3 + ky rows and 7 + kx columns), and frame
+// windows of neighbouring frames overlap, so a key region is loaded once for
+// the four frames.  Keys stream through LDS as units of 32 keys -- UR rows of
+// UC consecutive columns of one frame (2 x 16 when the patch's columns fit in
+// 16, else 1 x 32) -- in a ring of kNRing stages filled by direct global->LDS
+// loads kNRing - 1 units ahead.  A wave skips the products of units outside
+// its frame window; inside a unit, keys outside a query's window get
+// probability 0.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -23,20 +26,39 @@ namespace solattn {
 
 namespace {
 
-constexpr int kNU = 32;                  // keys per unit (one row segment)
+constexpr int kNU = 32;                  // keys per unit
 constexpr int kNUE = kNU * kHeadDim;     // bf16 per tensor per stage
-constexpr int kNRing = 3;
-constexpr int kNDma = 4;                 // loads per wave per unit (K and V, 2 x 4 rows each)
-constexpr int kNWaitNext = (kNDma & 15) | 0x0F70;  // vmcnt(4): the next unit landed
+constexpr int kNRing = 4;
+constexpr int kNAhead = kNRing - 1;      // units in flight ahead of the one computed
+constexpr int kNDma = 4;                 // loads per wave per unit (K and V, 2 x 4 keys each)
+// vmcnt((kNAhead - 1) * kNDma): all of this wave's loads but those of the
+// kNAhead - 1 newest units have landed
+constexpr int kNWait = (((kNAhead - 1) * kNDma) & 15) | 0x0F70;
+static_assert((kNAhead - 1) * kNDma < 16, "vmcnt field");
+constexpr int kPR = 4, kPC = 8;          // query patch: rows x columns
 
 __device__ __forceinline__ int n_kslot(int row, int c) { return c ^ (row & 15); }
 __device__ __forceinline__ int n_vslot(int row, int c) { return c ^ ((row & 3) << 2); }
 
 __device__ __forceinline__ int win_start(int p, int len, int k) { return min(max(p - (k >> 1), 0), len - k); }
 
+constexpr float kSlack = 8.f;  // log2 units the reference may lag the row maximum
+
+// Direct global -> LDS load of 16 bytes per lane from sbase + voff (sbase
+// wave-uniform, voff a 32-bit per-lane byte offset); lane l's bytes land at
+// LDS byte address lds + 16 l.  Ordered by explicit vmcnt waits and barriers.
+__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
 }  // namespace
 
+template <int UR>
 __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
+  constexpr int UC = kNU / UR;  // columns per unit row
   __shared__ __attribute__((aligned(16))) u16 lds_k[kNRing][kNUE];
   __shared__ __attribute__((aligned(16))) u16 lds_v[kNRing][kNUE];
 
@@ -45,25 +67,33 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = a.T, Y = a.Y, X = a.X;
 
-  // brick: consecutive workgroups take neighbouring column bricks of a row band
-  const int bx_n = (X + 15) >> 4, by_n = (Y + 7) >> 3;
+  // Workgroup -> (head, frame group, patch).  Workgroups are dealt to the
+  // eight XCDs in turn; when their count allows, the order is remapped so
+  // that each XCD runs a contiguous range of patches (neighbours share keys
+  // through that XCD's L2).
+  const int px_n = (X + kPC - 1) / kPC, py_n = (Y + kPR - 1) / kPR, pt_n = (T + 3) >> 2;
+  const int total = px_n * py_n * pt_n * a.H;
   int b = blockIdx.x;
-  const int bx = b % bx_n;
-  b /= bx_n;
-  const int by = b % by_n;
-  const int t = b / by_n;
-  const int h = blockIdx.y;
-  const int x0 = bx * 16, y0 = by * 8;
+  if ((total & 7) == 0) b = (b & 7) * (total >> 3) + (b >> 3);
+  const int px = b % px_n;
+  b /= px_n;
+  const int py = b % py_n;
+  b /= py_n;
+  const int pt = b % pt_n;
+  const int h = b / pt_n;
+  const int x0 = px * kPC, y0 = py * kPR, f0 = pt * 4;
 
   // this lane's query
-  const int yq = y0 + 2 * wave + (r32 >> 4), xq = x0 + (r32 & 15);
-  const bool qvalid = yq < Y && xq < X;
+  const int fq = f0 + wave, yq = y0 + (r32 >> 3), xq = x0 + (r32 & 7);
+  const bool wvalid = fq < T;  // wave-uniform
+  const bool qvalid = wvalid && yq < Y && xq < X;
   const int64_t plane = (int64_t)Y * X;
-  const int64_t qrow = (int64_t)t * plane + (int64_t)min(yq, Y - 1) * X + min(xq, X - 1);
-  const u16* qh = a.q + (int64_t)h * T * plane * kHeadDim;
+  const int fqc = min(fq, T - 1), yqc = min(yq, Y - 1), xqc = min(xq, X - 1);
+  const int64_t qrow = (int64_t)fqc * plane + (int64_t)yqc * X + xqc;
+  const int64_t head = (int64_t)h * T * plane * kHeadDim;
   QFrag qf;
   {
-    const u32x4* p = reinterpret_cast<const u32x4*>(qh + qrow * kHeadDim);
+    const u32x4* p = reinterpret_cast<const u32x4*>(a.q + head + qrow * kHeadDim);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       u32x4 x = {0u, 0u, 0u, 0u};
@@ -71,62 +101,100 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
       qf.k[ks] = as_bf16x8(x);
     }
   }
-  // window of this lane's query (rows and columns; the frames of the brick's
-  // units are exactly the frame window)
-  const int wy = win_start(min(yq, Y - 1), Y, a.ky), wx = win_start(min(xq, X - 1), X, a.kx);
-  // rows any query of this wave sees (wave-uniform)
-  const int wy_lo = win_start(min(y0 + 2 * wave, Y - 1), Y, a.ky);
-  const int wy_hi = win_start(min(y0 + 2 * wave + 1, Y - 1), Y, a.ky) + a.ky;
-  // units of the brick
-  const int ts = win_start(t, T, a.kt);
+  // window of this lane's query
+  const int wy = win_start(yqc, Y, a.ky), wx = win_start(xqc, X, a.kx);
+  // frames of this wave's window (wave-uniform)
+  const int wf = win_start(fqc, T, a.kt);
+  // key region of the workgroup: frames [fa, fb), rows [ya, yb), columns from xu
+  const int fa = win_start(f0, T, a.kt);
+  const int fb = win_start(min(f0 + 3, T - 1), T, a.kt) + a.kt;
   const int ya = win_start(y0, Y, a.ky);
-  const int yb = win_start(min(y0 + 7, Y - 1), Y, a.ky) + a.ky;  // exclusive
+  const int yb = win_start(min(y0 + kPR - 1, Y - 1), Y, a.ky) + a.ky;
   const int xa = win_start(x0, X, a.kx);
-  const int xu = max(0, min(xa, X - kNU));  // first column of every unit
-  const int nrows = yb - ya;
-  const int nunits = a.kt * nrows;
+  const int xu = max(0, min(xa, X - UC));  // first column of every unit
+  const int nunits = (fb - fa) * ((yb - ya + UR - 1) / UR);
 
-  const u16* kh = a.k + (int64_t)h * T * plane * kHeadDim;
-  const u16* vh = a.v + (int64_t)h * T * plane * kHeadDim;
+  const char* kh = reinterpret_cast<const char*>(a.k + head);
+  const char* vh = reinterpret_cast<const char*>(a.v + head);
   __builtin_amdgcn_s_waitcnt(0);
 
-  // direct loads of unit u: wave w fills K and V rows 8w .. 8w+7 (columns
-  // xu + row, clamped to the last column: those keys are never in a window)
+  // Direct loads of a unit: wave w fills keys 8w .. 8w+7 (two groups of 4,
+  // K and V).  Key r of a unit is (row group start + r / UC, xu + r % UC); a
+  // lane's byte offset from the unit's first key is fixed for the whole
+  // kernel, so a unit costs only its scalar base.  Columns past the grid are
+  // clamped to the last one (never inside a window); the row group is moved
+  // up so that it ends inside the grid, and its rows before the nominal start
+  // are masked (they belong to the previous group).
   const int slot = lane & 15;
-  auto dma_unit = [&](int u, int st) __attribute__((always_inline)) {
-    u = min(u, nunits - 1);
-    const int tt = ts + u / nrows, yy = ya + u % nrows;
-    const int64_t base = (int64_t)tt * plane + (int64_t)yy * X;
+  uint32_t koff[2], voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = wave * 8 + i * 4 + (lane >> 4);
+    const uint32_t key = (uint32_t)((r / UC) * X + min(xu + r % UC, X - 1));
+    koff[i] = key * (kHeadDim * 2) + (n_kslot(r, slot) << 4);
+    voff[i] = key * (kHeadDim * 2) + (n_vslot(r, slot) << 4);
+  }
+  const int ylast = Y - UR;  // last start of a row group that stays in the grid
+  auto dma_unit = [&](int ff, int yy, int st) __attribute__((always_inline)) {
+    const int64_t base = ((int64_t)ff * plane + (int64_t)min(yy, ylast) * X) * (kHeadDim * 2);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r0 = wave * 8 + i * 4;
-      const int r = r0 + (lane >> 4);
-      const int64_t key = base + min(xu + r, X - 1);
-      dma_to_lds16(kh + key * kHeadDim + (n_kslot(r, slot) << 3), lds_addr(&lds_k[st][r0 * kHeadDim]));
-      dma_to_lds16(vh + key * kHeadDim + (n_vslot(r, slot) << 3), lds_addr(&lds_v[st][r0 * kHeadDim]));
+      dma16_sv(kh + base, koff[i], lds_addr(&lds_k[st][r0 * kHeadDim]));
+      dma16_sv(vh + base, voff[i], lds_addr(&lds_v[st][r0 * kHeadDim]));
     }
   };
 
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-  // two denominators: of the bf16 probabilities the PV product uses (the
-  // output's normaliser, so weights sum to one exactly as multiplied) and of
-  // the fp32 exponentials (for lse: with windows of a few dozen keys the bf16
-  // rounding of p would not average out)
-  float l = 0.f, l32 = 0.f, m = -__builtin_inff();
+  // Running sums relative to a reference m (log2 units) that may lag the row
+  // maximum by up to kSlack: o and l are rescaled only when the maximum
+  // outruns it.  Two denominators: of the bf16 probabilities the PV product
+  // uses (the output's normaliser, so the weights sum to one exactly as
+  // multiplied) and of the fp32 exponentials (for lse: with windows of a few
+  // dozen keys the bf16 rounding of p would not average out).  m starts at a
+  // finite -1e30, so that a unit without keys of this query (maximum -inf)
+  // leaves it alone and its probabilities come out 0.
+  float l = 0.f, l32 = 0.f, m = -1e30f;
   const float sl2 = 0.08838834764831845f * kLog2e;
+  // column mask of element i (key column xu + acc_row(i, 0) % UC + 4g), as an
+  // additive 0 / -inf bias fixed for the kernel; elements i and i + 16 / UR
+  // share a column
+  constexpr int NC = 16 / UR;
+  float cbias[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = xu + acc_row(i, 0) % UC + g4;
+    cbias[i] = (c >= wx && c < wx + a.kx) ? 0.f : -__builtin_inff();
+  }
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
 
-  dma_unit(0, 0);
-  dma_unit(1, 1);
+  // unit counters (frame, nominal row-group start) of the loads and of the
+  // products, advanced without divisions
+  int lf = fa, ly = ya, cf = fa, cy = ya;
+  auto advance = [&](int& f, int& y) __attribute__((always_inline)) {
+    y += UR;
+    if (y >= yb) { y = ya; ++f; }
+  };
+#pragma unroll
+  for (int i = 0; i < kNAhead; ++i) {
+    dma_unit(min(lf, fb - 1), lf < fb ? ly : yb - 1, i);
+    advance(lf, ly);
+  }
   for (int u = 0; u < nunits; ++u) {
     const int st = u % kNRing;
-    __builtin_amdgcn_s_waitcnt(kNWaitNext);  // this wave's loads of unit u landed
-    __builtin_amdgcn_s_barrier();            // ... and every wave's; unit u - 1's stage is free
+    __builtin_amdgcn_s_waitcnt(kNWait);  // this wave's loads of unit u landed
+    __builtin_amdgcn_s_barrier();        // ... and every wave's; unit u - 1's stage is free
     asm volatile("" ::: "memory");
-    dma_unit(u + 2, (u + 2) % kNRing);       // past the end: re-loads the last unit (never read)
-    const int yy = ya + u % nrows;
-    if (yy < wy_lo || yy >= wy_hi) continue;  // wave-uniform: no query of this wave sees the row
+    // past the end: re-loads the last unit into a stage that is never read
+    dma_unit(min(lf, fb - 1), lf < fb ? ly : yb - 1, (u + kNAhead) % kNRing);
+    advance(lf, ly);
+    const int ff = cf, ynom = cy;
+    advance(cf, cy);
+    if (!wvalid || ff < wf || ff >= wf + a.kt) continue;  // wave-uniform
+    const int yy = min(ynom, ylast);
 
     // S^T = K Q^T for the unit's 32 keys
     f32x16 s = {};
@@ -135,40 +203,50 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
       const u32x4 kf = *reinterpret_cast<const u32x4*>(&lds_k[st][r32 * kHeadDim + (n_kslot(r32, ks * 2 + g) << 3)]);
       s = mfma32(as_bf16x8(kf), qf.k[ks], s);
     }
-    // keys outside this query's window: row test once, column test per key
-    // (element i holds key column xu + acc_row(i, 0) + 4g)
-    const bool row_in = yy >= wy && yy < wy + a.ky;
-    const int lo = wx - xu - g4, hi = wx + a.kx - xu - g4;  // acc_row(i,0) in [lo, hi)
-    float mx = -__builtin_inff();
+    // rows of the unit inside this query's window (and not before the group's
+    // nominal start)
+    const int rlo = max(wy, ynom), rhi = wy + a.ky;
+    float mxr[UR];
+#pragma unroll
+    for (int rr = 0; rr < UR; ++rr) mxr[rr] = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int c = acc_row(i, 0);
-      if (!row_in || c < lo || c >= hi) s[i] = -__builtin_inff();
-      mx = fmaxf(mx, s[i]);
+      s[i] += cbias[i % NC];
+      mxr[acc_row(i, 0) / UC] = fmaxf(mxr[acc_row(i, 0) / UC], s[i]);
+    }
+    float rbias[UR], mx = -__builtin_inff();
+#pragma unroll
+    for (int rr = 0; rr < UR; ++rr) {
+      rbias[rr] = (yy + rr >= rlo && yy + rr < rhi) ? 0.f : -__builtin_inff();
+      mx = fmaxf(mx, mxr[rr] + rbias[rr]);
     }
     // partner lane l ^ 32 holds the other 16 keys of the same query
     const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-    const float mn = fmaxf(m, mx * sl2);
-    const float base = mn == -__builtin_inff() ? 0.f : mn;
-    const bool up = mn > m;
+    const float mc = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * sl2;
+    const bool up = mc > m + kSlack;
     if (__ballot(up)) {
-      const float alpha = fast_exp2(m - base);
+      const float alpha = up ? fast_exp2(m - mc) : 1.f;
       l *= alpha;
       l32 *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
-    m = mn;
+    if (up) m = mc;
+    float nref[UR];
+#pragma unroll
+    for (int rr = 0; rr < UR; ++rr) nref[rr] = rbias[rr] - m;
     bf16x8 pb[2];
     float rs = 0.f, rs32 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = fast_exp2(__builtin_fmaf(s[i], sl2, -base));
-      const __bf16 p = (__bf16)e;
-      pb[i >> 3][i & 7] = p;
-      rs += (float)p;
-      rs32 += e;
+    for (int i = 0; i < 16; i += 2) {
+      const float e0 = fast_exp2(__builtin_fmaf(s[i], sl2, nref[acc_row(i, 0) / UC]));
+      const float e1 = fast_exp2(__builtin_fmaf(s[i + 1], sl2, nref[acc_row(i + 1, 0) / UC]));
+      const __bf16 b0 = (__bf16)e0, b1 = (__bf16)e1;
+      pb[i >> 3][i & 7] = b0;
+      pb[i >> 3][(i & 7) + 1] = b1;
+      const bf16x2 pr2 = {b0, b1};
+      rs = __builtin_amdgcn_fdot2_f32_bf16(pr2, one2, rs, false);
+      rs32 += e0 + e1;
     }
     l += rs;
     l32 += rs32;
@@ -196,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
   const float lt32 = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
   if (!qvalid) return;
   const float inv = 1.f / lt;
-  u16* orow = a.out + ((int64_t)h * T * plane + qrow) * kHeadDim;
+  u16* orow = a.out + head + qrow * kHeadDim;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -211,8 +289,13 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
 }
 
 hipError_t launch_na3d(const Na3dArgs& a, hipStream_t s) {
-  const int bricks = ((a.X + 15) / 16) * ((a.Y + 7) / 8) * a.T;
-  na3d_kernel<<<dim3(bricks, a.H), 256, 0, s>>>(a);
+  const int wgs = ((a.X + kPC - 1) / kPC) * ((a.Y + kPR - 1) / kPR) * ((a.T + 3) / 4) * a.H;
+  // the patch's key columns (at most kPC - 1 + kx) fit in a 16-column unit
+  // row (and the grid has the two rows of a unit)
+  if (kPC - 1 + a.kx <= 16 && a.Y >= 2)
+    na3d_kernel<2><<<wgs, 256, 0, s>>>(a);
+  else
+    na3d_kernel<1><<<wgs, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

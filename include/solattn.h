@@ -227,7 +227,7 @@ int fp8_gemm_rowscale(const uint8_t* a, const float* sa, const uint8_t* w, const
  * q, k, v  [H, T*Y*X, d] bf16 (read), tokens frame-major then row-major.
  * out      [H, T*Y*X, d] bf16 (written).  lse [H, T*Y*X] fp32 (may be NULL).
  * kt, ky, kx odd and at most T, Y, X (SOL_ERR_INVALID_ARG otherwise);
- * d = 128 and kx <= 17 (SOL_ERR_UNSUPPORTED otherwise).  16-byte alignment.
+ * d = 128 and kx <= 25 (SOL_ERR_UNSUPPORTED otherwise).  16-byte alignment.
  */
 int na3d_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
                  float* lse, int T, int Y, int X, int H, int d, int kt, int ky, int kx,

@@ -87,7 +87,7 @@ def test_other_entry_points_argument_errors(lib):
     assert na(N, FAKE, FAKE, FAKE, N, 2, 8, 8, 1, 128, 1, 3, 3, N) == -1        # null q
     assert na(FAKE, FAKE, FAKE, FAKE, N, 2, 8, 8, 1, 128, 2, 3, 3, N) == -1     # even window
     assert na(FAKE, FAKE, FAKE, FAKE, N, 2, 8, 8, 1, 128, 3, 3, 3, N) == -1     # window > T
-    assert na(FAKE, FAKE, FAKE, FAKE, N, 2, 8, 40, 1, 128, 1, 3, 19, N) == -2   # kx > 17
+    assert na(FAKE, FAKE, FAKE, FAKE, N, 2, 8, 40, 1, 128, 1, 3, 27, N) == -2   # kx > 25
     assert na(FAKE, FAKE, FAKE, FAKE, N, 2, 8, 8, 1, 64, 1, 3, 3, N) == -2      # d != 128
     assert lib.fp8_quantize_rows(N, FAKE, FAKE, ctypes.c_int64(4), 128, N) == -1
     assert lib.fp8_quantize_rows(FAKE, FAKE, FAKE, ctypes.c_int64(4), 12, N) == -2  # K % 8
