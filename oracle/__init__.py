@@ -62,6 +62,7 @@ __all__ = [
     "dense_head_ref",
     "lse_merge_ref",
     "sol_attn_ref",
+    "sol_attn_shard_ref",
     "dense_ref",
 ]
 
@@ -136,7 +137,8 @@ def near_ties_ref(p: np.ndarray, mu: np.ndarray, sigma: np.ndarray, beta: float,
 def sol_attn_head_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int,
                       beta: float, rows: Optional[Sequence[int]] = None,
                       force: Optional[dict] = None, taylor: bool = True,
-                      chunk: int = 256, pooled=None):
+                      chunk: int = 256, pooled=None,
+                      blocks: Optional[Sequence[int]] = None):
     """One head of Sol-Attn-style sparse attention, step by step [SOL].
 
     ``q`` ``[nq, d]``, ``k``/``v`` ``[nk, d]`` (float64).  ``rows`` restricts
@@ -146,9 +148,19 @@ def sol_attn_head_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int,
     ``(kbar, vbar)`` this function returned in ``info`` for the same keys, to
     skip recomputing them.
 
+    ``blocks`` restricts the exact and the Taylor sums to those key blocks --
+    one rank's share of keys split along the sequence [DAI "Attention across
+    two GPUs": each GPU attends to its part of the keys and the partial
+    answers merge] -- while the proxy statistics ``mu``, ``sigma`` still run
+    over every block of ``k`` (the thresholds of the whole sequence [SOL]).
+    The result is then that share's partial answer: ``out`` = its numerator
+    over its denominator, ``lse`` = reference + log of its denominator.
+
     Returns ``(out [R, d], lse [R], info)`` where ``info`` holds ``p``, ``mu``,
-    ``sigma`` and the selection ``mask`` of the computed rows.  A row whose
-    denominator is not positive gets NaN output (none occur on the workloads).
+    ``sigma``, the selection ``mask`` of the computed rows and ``partial`` =
+    ``(num [R, d], den [R], M [R])`` (``num``, ``den`` relative to ``e^M``).
+    A row whose denominator is not positive gets NaN output (none occur on the
+    workloads; a share of rejected blocks alone can have one).
     """
     nq, d = q.shape
     nk = k.shape[0]
@@ -174,6 +186,16 @@ def sol_attn_head_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int,
         local_force = {(pos[r], j): val for (r, j), val in force.items() if r in pos}
     sel = select_ref(p, mu, sigma, beta, local_force)
     tok_block = np.repeat(np.arange(len(bounds)), n_j.astype(np.int64))
+    # blocks whose keys this computation sums over (all, or one share)
+    in_share = np.ones(len(bounds), dtype=bool)
+    if blocks is not None:
+        in_share[:] = False
+        in_share[np.asarray(blocks, dtype=np.int64)] = True
+    sel_in = sel & in_share[None, :]
+    rej_in = ~sel & in_share[None, :]
+    pnum = np.empty((len(rows), d))
+    pden = np.empty(len(rows))
+    pM = np.empty(len(rows))
 
     out = np.empty((len(rows), d))
     lse = np.empty(len(rows))
@@ -181,11 +203,11 @@ def sol_attn_head_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int,
         r1 = min(len(rows), r0 + chunk)
         # step 5: exact logits
         s = scale * (qr[r0:r1] @ k.T)                      # [R, nk]
-        tok_sel = sel[r0:r1][:, tok_block]                  # [R, nk]
+        tok_sel = sel_in[r0:r1][:, tok_block]               # [R, nk]
         # step 6: reference shift (any finite shift is exact; this one avoids overflow)
         s_sel = np.where(tok_sel, s, -np.inf)
         M = s_sel.max(axis=1)
-        any_rej = (~sel[r0:r1]).any(axis=1)
+        any_rej = rej_in[r0:r1].any(axis=1)
         M = np.where(any_rej & taylor, np.maximum(M, mu[r0:r1]), M)
         # step 7: exact part over selected blocks ...
         with np.errstate(invalid="ignore", over="ignore"):
@@ -196,15 +218,17 @@ def sol_attn_head_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int,
         if taylor:
             dmu = p[r0:r1] - mu[r0:r1, None]
             w = n_j[None, :] * np.exp(mu[r0:r1] - M)[:, None] * (1.0 + dmu)
-            w = np.where(sel[r0:r1], 0.0, w)
+            w = np.where(rej_in[r0:r1], w, 0.0)
             num = num + w @ vbar
             den = den + w.sum(axis=1)
+        pnum[r0:r1], pden[r0:r1], pM[r0:r1] = num, den, M
         # step 8: normalise
         ok = den > 0
         with np.errstate(invalid="ignore", divide="ignore"):
             out[r0:r1] = np.where(ok[:, None], num / den[:, None], np.nan)
             lse[r0:r1] = np.where(ok, M + np.log(np.where(ok, den, 1.0)), np.nan)
-    info = dict(p=p, mu=mu, sigma=sigma, mask=sel, rows=rows, pooled=(kbar, vbar))
+    info = dict(p=p, mu=mu, sigma=sigma, mask=sel, rows=rows, pooled=(kbar, vbar),
+                partial=(pnum, pden, pM))
     return out, lse, info
 
 
@@ -255,6 +279,20 @@ def sol_attn_ref(Q, K, V, B: int, beta: float, rows=None, taylor: bool = True):
     outs, lses = [], []
     for q, k, v in zip(_heads(Q), _heads(K), _heads(V)):
         o, l, _ = sol_attn_head_ref(q, k, v, B, beta, rows=rows, taylor=taylor)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
+def sol_attn_shard_ref(Q, K, V, B: int, beta: float, blocks: Sequence[int], rows=None):
+    """All heads of one share's partial answer (``blocks`` of the key sequence,
+    statistics over all blocks); ``(out, lse)`` stacked over heads."""
+    Q = Q if Q.dtype != np.uint16 else bf16_to_f64(Q)
+    K = K if K.dtype != np.uint16 else bf16_to_f64(K)
+    V = V if V.dtype != np.uint16 else bf16_to_f64(V)
+    outs, lses = [], []
+    for q, k, v in zip(_heads(Q), _heads(K), _heads(V)):
+        o, l, _ = sol_attn_head_ref(q, k, v, B, beta, rows=rows, blocks=blocks)
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses)
