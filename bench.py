@@ -137,6 +137,52 @@ def fp8_projection(sa, torch, tokens, hidden, dev, stream, reps=5):
             "pct_fp8_peak": 100 * flops / g_ms / 1e9 / PEAK_FP8_TFLOPS}
 
 
+def kv_sharded(sa, torch, q, k, v, B, beta, stream, dense_flops, unsplit_ms, ranks=2, reps=3):
+    """Key-sharded Sol-Attn at 4K on one GPU: each rank's share of whole key
+    blocks (its keys against every query, thresholds from the pooled keys of
+    every block), run one after another, and the exact merge of the shares.
+    In a deployment each share runs on its own GPU; the exchange of pooled
+    keys and partial answers is not timed here."""
+    H, N, d = q.shape
+    nb = (N + B - 1) // B
+    cuts = [round(i * nb / ranks) for i in range(ranks + 1)]
+    kbar_all, _ = sa.sol_attn_pool(k, v, B)
+    shares = []
+    for r in range(ranks):
+        lo, hi = cuts[r] * B, min(N, cuts[r + 1] * B)
+        shares.append((k[:, lo:hi].contiguous(), v[:, lo:hi].contiguous()))
+    part_o = torch.empty((ranks, H, N, d), dtype=torch.float32, device=q.device)
+    part_ml = torch.empty((ranks, H, N, 2), dtype=torch.float32, device=q.device)
+    wss = [torch.empty(max(1, sa.sol_attn_shard_workspace_size(N, ks.shape[1], nb, H, d, B, beta)),
+                       dtype=torch.uint8, device=q.device) for ks, _ in shares]
+    out = torch.empty_like(q)
+
+    def run(ev=None):
+        for r, (ks, vs) in enumerate(shares):
+            sa.sol_attn_forward_shard(q, ks, vs, kbar_all, B=B, beta=beta, part_o=part_o[r],
+                                      part_ml=part_ml[r], workspace=wss[r])
+            if ev is not None:
+                ev[r + 1].record(stream)
+        sa.sol_attn_combine_partials(part_o, part_ml, out=out)
+        if ev is not None:
+            ev[ranks + 1].record(stream)
+
+    run()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(ranks + 2)]
+        ev[0].record(stream)
+        run(ev)
+        torch.cuda.synchronize()
+        times.append([ev[i].elapsed_time(ev[i + 1]) for i in range(ranks + 1)])
+    t = np.median(np.array(times), axis=0)
+    return {"ranks": ranks, "blocks_per_rank": [cuts[r + 1] - cuts[r] for r in range(ranks)],
+            "share_ms": [float(x) for x in t[:ranks]], "combine_ms": float(t[ranks]),
+            "sum_ms": float(t.sum()), "unsplit_ms": unsplit_ms,
+            "per_rank_dense_equiv_tflops": dense_flops / ranks / float(np.max(t[:ranks])) / 1e9}
+
+
 def na3d_decoder_tile(sa, torch, dev, stream, reps=10):
     """3D neighbourhood attention over one decoder tile of four latent frames
     of the 4K grid (4 x 68 x 120 tokens), 16 heads of 128, window 3 x 7 x 7
@@ -337,6 +383,8 @@ def main():
         ms = es[0].elapsed_time(es[1]) / 2
         extras["4k_dense"] = {"ms_per_call": ms, "tflops": dense_flops / ms / 1e9,
                               "pct_bf16_peak": 100 * dense_flops / ms / 1e9 / PEAK_BF16_TFLOPS}
+        extras["4k_sparse_kv_sharded"] = kv_sharded(sa, torch, q, k, v, B, args.beta, stream,
+                                                    dense_flops, call_ms)
         extras["fp8_projection_4k"] = fp8_projection(sa, torch, N, H * d, q.device, stream)
         extras["na3d_decoder_tile_4k"] = na3d_decoder_tile(sa, torch, q.device, stream)
 

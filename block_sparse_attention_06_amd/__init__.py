@@ -37,6 +37,9 @@ __all__ = [
     "fp8_quantize_rows",
     "fp8_gemm_rowscale",
     "na3d_forward",
+    "sol_attn_forward_shard",
+    "sol_attn_shard_workspace_size",
+    "sol_attn_combine_partials",
 ]
 
 SOL_DENSE = 0
@@ -86,6 +89,9 @@ def load_library() -> ctypes.CDLL:
         "fp8_quantize_rows": (I, [P, P, P, L, I, P]),
         "fp8_gemm_rowscale": (I, [P, P, P, P, P, I, I, I, P]),
         "na3d_forward": (I, [P, P, P, P, P, I, I, I, I, I, I, I, I, P]),
+        "sol_attn_forward_shard": (I, [P, P, P, P, P, P, I, I, I, I, I, I, F, P, S, P]),
+        "sol_attn_shard_workspace_size": (S, [I, I, I, I, I, I, F]),
+        "sol_attn_combine_partials": (I, [P, P, I, P, P, I, I, I, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -229,6 +235,71 @@ def attn_lse_merge(out_a: torch.Tensor, lse_a: torch.Tensor, out_b: torch.Tensor
     _check("attn_lse_merge", lib.attn_lse_merge(
         _ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), _ptr(out), _ptr(lse), N, H, d,
         _stream(stream)))
+    return out, lse
+
+
+def sol_attn_shard_workspace_size(N: int, Nk: int, nb_all: int, H: int, d: int, B: int,
+                                  beta: float) -> int:
+    return int(load_library().sol_attn_shard_workspace_size(N, Nk, nb_all, H, d, B,
+                                                             float(beta)))
+
+
+def sol_attn_forward_shard(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           kbar_all: Optional[torch.Tensor], B: int = 128, beta: float = 0.5,
+                           part_o: Optional[torch.Tensor] = None,
+                           part_ml: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None):
+    """One rank's share of key-sharded Sol-Attn: the partial answer of every
+    query row over the key blocks in ``k``/``v`` (whole blocks of the full
+    sequence), with thresholds from ``kbar_all`` ``[H, nb_all, 128]`` (the
+    pooled keys of every block).  Returns ``(part_o [H,N,128] fp32,
+    part_ml [H,N,2] fp32)``; merge shares with :func:`sol_attn_combine_partials`."""
+    lib = load_library()
+    _want(q, "q", torch.bfloat16, 3)
+    _want(k, "k", torch.bfloat16, 3)
+    _want(v, "v", torch.bfloat16, 3)
+    H, N, d = q.shape
+    Nk = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != H or k.shape[2] != d:
+        raise ValueError("k and v must be [H, Nk, d] with q's H and d")
+    if math.isnan(beta):
+        raise ValueError("beta must not be NaN")
+    nb_all = 0
+    if kbar_all is not None:
+        _want(kbar_all, "kbar_all", torch.float32, 3)
+        nb_all = kbar_all.shape[1]
+    if part_o is None:
+        part_o = torch.empty((H, N, d), dtype=torch.float32, device=q.device)
+    if part_ml is None:
+        part_ml = torch.empty((H, N, 2), dtype=torch.float32, device=q.device)
+    _want(part_o, "part_o", torch.float32, 3)
+    _want(part_ml, "part_ml", torch.float32, 3)
+    ws_bytes = sol_attn_shard_workspace_size(N, Nk, nb_all, H, d, B, beta)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("sol_attn_forward_shard", lib.sol_attn_forward_shard(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(kbar_all), _ptr(part_o), _ptr(part_ml), N, Nk, nb_all,
+        H, d, int(B), float(beta), _ptr(workspace), have, _stream(stream)))
+    return part_o, part_ml
+
+
+def sol_attn_combine_partials(part_o: torch.Tensor, part_ml: torch.Tensor,
+                              out: Optional[torch.Tensor] = None, want_lse: bool = True,
+                              stream=None):
+    """Exact merge of S partial answers ``part_o [S,H,N,128]``, ``part_ml [S,H,N,2]``
+    (fp32); returns ``(out [H,N,128] bf16, lse [H,N] fp32 or None)``."""
+    lib = load_library()
+    _want(part_o, "part_o", torch.float32, 4)
+    _want(part_ml, "part_ml", torch.float32, 4)
+    S, H, N, d = part_o.shape
+    if tuple(part_ml.shape) != (S, H, N, 2):
+        raise ValueError("part_ml must be [S, H, N, 2]")
+    if out is None:
+        out = torch.empty((H, N, d), dtype=torch.bfloat16, device=part_o.device)
+    lse = torch.empty((H, N), dtype=torch.float32, device=part_o.device) if want_lse else None
+    _check("sol_attn_combine_partials", lib.sol_attn_combine_partials(
+        _ptr(part_o), _ptr(part_ml), S, _ptr(out), _ptr(lse), N, H, d, _stream(stream)))
     return out, lse
 
 

@@ -97,6 +97,46 @@ Plan make_plan(int N, int Nk, int H, int B, int mode) {
   return p;
 }
 
+// Workspace of one key share (sol_attn_forward_shard): the pooled local
+// blocks and their routing forms, mu and sigma of every row, and the moment
+// buffers when the whole sequence has kMomentMinBlocks blocks or more.  No key
+// split inside a share, so no partial buffers.
+struct ShardPlan {
+  int nb, nb_pad;
+  size_t off_kbar, off_vbar, off_vsum, off_khi, off_klo, off_mu, off_sigma;
+  size_t off_chi, off_clo, off_mbar, bytes;
+  bool moments;
+};
+
+ShardPlan make_shard_plan(int N, int Nk, int nb_all, int H, int B, bool sparse) {
+  ShardPlan p{};
+  p.nb = cdiv(Nk, sparse ? B : 128);
+  p.nb_pad = (int)round_up((size_t)p.nb, 32);
+  if (!sparse) return p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  const size_t HN = (size_t)H * N;
+  p.off_kbar = take((size_t)H * p.nb * 128 * sizeof(float));
+  p.off_vbar = take((size_t)H * p.nb * 128 * sizeof(float));
+  p.off_vsum = take((size_t)H * 128 * p.nb_pad * sizeof(uint16_t));
+  p.off_khi = take((size_t)H * p.nb_pad * 128 * sizeof(uint16_t));
+  p.off_klo = take((size_t)H * p.nb_pad * 128 * sizeof(uint16_t));
+  p.off_mu = take(HN * sizeof(float));
+  p.off_sigma = take(HN * sizeof(float));
+  p.moments = nb_all >= kMomentMinBlocks;
+  if (p.moments) {
+    p.off_chi = take((size_t)H * 128 * 128 * sizeof(uint16_t));
+    p.off_clo = take((size_t)H * 128 * 128 * sizeof(uint16_t));
+    p.off_mbar = take((size_t)H * 128 * sizeof(float));
+  }
+  p.bytes = off;
+  return p;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? SOL_OK : SOL_ERR_HIP; }
 
 int check_shape(int N, int H, int d) {
@@ -275,6 +315,76 @@ int sol_attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, ui
     if (int r = hip_status(launch_combine(c, s))) return r;
   }
   return SOL_OK;
+}
+
+size_t sol_attn_shard_workspace_size(int N, int Nk, int nb_all, int H, int d, int B,
+                                     float beta) {
+  if (N <= 0 || Nk <= 0 || H <= 0 || d != 128 || check_block(B) || isnan(beta)) return 0;
+  const bool sparse = !(isinf(beta) && beta < 0);
+  if (sparse && nb_all < cdiv(Nk, B)) return 0;
+  return make_shard_plan(N, Nk, nb_all, H, B, sparse).bytes;
+}
+
+int sol_attn_forward_shard(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const float* kbar_all, float* part_o, float* part_ml, int N,
+                           int Nk, int nb_all, int H, int d, int B, float beta,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !part_o || !part_ml) return SOL_ERR_INVALID_ARG;
+  if (int r = check_shape(N, H, d)) return r;
+  if (Nk <= 0) return SOL_ERR_INVALID_ARG;
+  if (int r = check_block(B)) return r;
+  if (isnan(beta)) return SOL_ERR_INVALID_ARG;
+  const bool sparse = !(isinf(beta) && beta < 0);
+  if (sparse && (!kbar_all || nb_all < cdiv(Nk, B) || !aligned(kbar_all, 16)))
+    return SOL_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(part_o, 16) ||
+      !aligned(part_ml, 8))
+    return SOL_ERR_INVALID_ARG;
+  const ShardPlan p = make_shard_plan(N, Nk, nb_all, H, B, sparse);
+  if (p.bytes > 0 && (!workspace || ws_bytes < p.bytes || !aligned(workspace, 256)))
+    return SOL_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+
+  FwdArgs f{};
+  f.q = q; f.k = k; f.v = v; f.out = nullptr; f.lse = nullptr;
+  f.beta = beta; f.N = N; f.Nk = Nk; f.H = H;
+  f.nb = p.nb; f.nb_pad = p.nb_pad;
+  f.n_qt = cdiv(N, 128);
+  f.splits = 1; f.tiles_per_split = p.nb;
+  f.total = H * f.n_qt;
+  f.part_o = part_o; f.part_ml = part_ml;
+  if (sparse) {
+    // local blocks pooled for routing and the Taylor term; thresholds from
+    // the pooled keys of the whole sequence
+    PoolArgs pa{k, v, (float*)(ws + p.off_kbar), (float*)(ws + p.off_vbar),
+                (uint16_t*)(ws + p.off_vsum), (uint16_t*)(ws + p.off_khi),
+                (uint16_t*)(ws + p.off_klo), Nk, H, B, p.nb, p.nb_pad};
+    if (int r = hip_status(launch_pool(pa, s))) return r;
+    float* mu = (float*)(ws + p.off_mu);
+    float* sigma = (float*)(ws + p.off_sigma);
+    if (p.moments) {
+      MomentArgs ma{kbar_all, (uint16_t*)(ws + p.off_chi), (uint16_t*)(ws + p.off_clo),
+                    (float*)(ws + p.off_mbar), H, nb_all};
+      if (int r = hip_status(launch_moments(ma, s))) return r;
+      StatsMomentArgs sm{q, ma.chi, ma.clo, ma.mbar, mu, sigma, N, H};
+      if (int r = hip_status(launch_stats_moment(sm, s))) return r;
+    } else {
+      StatsArgs sa{q, kbar_all, mu, sigma, N, H, nb_all};
+      if (int r = hip_status(launch_stats(sa, s))) return r;
+    }
+    f.khi = pa.khi; f.klo = pa.klo; f.vsumT = pa.vsumT; f.mu = mu; f.sigma = sigma;
+  }
+  return hip_status(launch_forward(f, sparse, sparse ? B : 128, s));
+}
+
+int sol_attn_combine_partials(const float* part_o, const float* part_ml, int S, uint16_t* out,
+                              float* lse, int N, int H, int d, void* stream) {
+  if (!part_o || !part_ml || !out || S <= 0) return SOL_ERR_INVALID_ARG;
+  if (int r = check_shape(N, H, d)) return r;
+  if (!aligned(part_o, 16) || !aligned(part_ml, 8) || !aligned(out, 16)) return SOL_ERR_INVALID_ARG;
+  CombineArgs c{part_o, part_ml, out, lse, N, H, S};
+  return hip_status(launch_combine(c, (hipStream_t)stream));
 }
 
 int attn_lse_merge(const uint16_t* out_a, const float* lse_a, const uint16_t* out_b,

@@ -485,7 +485,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   // ---- epilogue ----
   const float lt = l + partner_f(l, g);
   if (!qvalid) return;
-  if (a.splits == 1) {
+  if (a.splits == 1 && !a.part_o) {
     const float inv = 1.f / lt;
     u16* orow = a.out + ((int64_t)h * a.N + row) * kHeadDim;
 #pragma unroll

@@ -102,7 +102,7 @@ struct FwdArgs {
   const uint16_t* vsumT;
   const float* mu;
   const float* sigma;
-  float* part_o;       // [S, H, N, 128] when S > 1
+  float* part_o;       // [S, H, N, 128] when S > 1, or a key share's partial (S = 1)
   float* part_ml;      // [S, H, N, 2]   (max in log2 units, denominator)
   float beta;
   int N, Nk, H;

@@ -158,6 +158,53 @@ int attn_lse_merge(const uint16_t* out_a, const float* lse_a, const uint16_t* ou
                    const float* lse_b, uint16_t* out, float* lse, int N, int H, int d,
                    void* stream);
 
+/*
+ * Key-sharded Sol-Attn, one rank's share: the partial answer of all N query
+ * rows over this rank's key blocks.
+ *   doubleAI page, "Attention across two GPUs": the keys are split along the
+ *   sequence, each GPU attends to its part, and the partial answers (each
+ *   with its running maximum and sum of exponentials) merge exactly.
+ *   Sol-Engine LTX25 page, "Stage 2 Optimization -- Core Technology:
+ *   Sol-Attn": a row's threshold comes from the proxy statistics of the
+ *   whole sequence, so every share uses the same mu_i, sigma_i; the exact and
+ *   the Taylor parts are sums over key blocks, so the shares add up exactly.
+ * q        [H, N, d] bf16: every query row (read).
+ * k, v     [H, Nk, d] bf16 (read): this rank's keys, whole key blocks of B of
+ *          the full sequence starting at a block boundary (only the last rank's
+ *          share may end in a ragged block).
+ * kbar_all [H, nb_all, d] fp32 (read): the pooled keys of every block of the
+ *          full sequence (each rank's sol_attn_pool output, gathered), used for
+ *          mu_i and sigma_i.  Ignored (may be NULL) when beta = -inf.
+ * part_o   [H, N, d] fp32 (written): the share's numerator relative to 2^m.
+ * part_ml  [H, N, 2] fp32 (written): m (log2 units) and the share's signed
+ *          denominator relative to 2^m (a share of rejected blocks alone can
+ *          have a negative one; the merge stays exact).
+ * beta     as sol_attn_forward (SOL_SPARSE); -inf gives the dense partial.
+ * workspace, ws_bytes: at least sol_attn_shard_workspace_size(...) bytes,
+ *          256-byte aligned (may be NULL when that size is 0).
+ * The share runs without a further key split inside the call.  16-byte
+ * aligned pointers (part_ml: 8).  Merge shares with sol_attn_combine_partials.
+ */
+int sol_attn_forward_shard(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const float* kbar_all, float* part_o, float* part_ml, int N,
+                           int Nk, int nb_all, int H, int d, int B, float beta,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace sol_attn_forward_shard needs (0 if none). */
+size_t sol_attn_shard_workspace_size(int N, int Nk, int nb_all, int H, int d, int B,
+                                     float beta);
+
+/*
+ * Exact merge of S partial answers in (numerator, m, denominator) form.
+ *   doubleAI page, "Attention across two GPUs".
+ * part_o   [S, H, N, d] fp32 and part_ml [S, H, N, 2] fp32 (read): share s at
+ *          index s (e.g. gathered from S ranks' sol_attn_forward_shard).
+ * out      [H, N, d] bf16 (written): sum_s 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s.
+ * lse      [H, N] fp32 natural log of the merged denominator, or NULL.
+ */
+int sol_attn_combine_partials(const float* part_o, const float* part_ml, int S, uint16_t* out,
+                              float* lse, int N, int H, int d, void* stream);
+
 /* Static description of a return code (never NULL). */
 const char* sol_attn_error_string(int code);
 

@@ -29,7 +29,9 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ("sol_attn_pool", "sol_attn_forward", "attn_lse_merge", "sol_attn_row_stats",
               "sol_attn_row_stats_moment", "sol_attn_workspace_size", "sol_attn_error_string", "sol_attn_proxy_scores",
-              "sol_attn_block_mask", "fp8_quantize_rows", "fp8_gemm_rowscale", "na3d_forward"):
+              "sol_attn_block_mask", "fp8_quantize_rows", "fp8_gemm_rowscale", "na3d_forward",
+              "sol_attn_forward_shard", "sol_attn_shard_workspace_size",
+              "sol_attn_combine_partials"):
         assert n in names
 
 
@@ -102,6 +104,28 @@ def test_other_entry_points_argument_errors(lib):
                                    N, FAKE, N) == -1          # row0 not a multiple of 128
     assert lib.sol_attn_block_mask(FAKE, FAKE, FAKE, FAKE, math.nan, 0, 10, 256, 256, 1, 128,
                                    64, N, FAKE, N) == -1
+
+
+def test_shard_entry_points_argument_errors(lib):
+    N = None
+    sh = lib.sol_attn_forward_shard
+    need = lib.sol_attn_shard_workspace_size(256, 128, 4, 1, 128, 64, 0.5)
+    assert need > 0
+    # (q, k, v, kbar_all, part_o, part_ml, N, Nk, nb_all, H, d, B, beta, ws, ws_bytes, stream)
+    assert sh(N, FAKE, FAKE, FAKE, FAKE, FAKE, 256, 128, 4, 1, 128, 64, 0.5, FAKE, need, N) == -1
+    assert sh(FAKE, FAKE, FAKE, N, FAKE, FAKE, 256, 128, 4, 1, 128, 64, 0.5, FAKE, need, N) == -1  # no kbar_all
+    assert sh(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, 128, 1, 1, 128, 64, 0.5, FAKE, need, N) == -1  # nb_all < local blocks
+    assert sh(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, 0, 4, 1, 128, 64, 0.5, FAKE, need, N) == -1
+    assert sh(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, 128, 4, 1, 128, 64, math.nan, FAKE, need, N) == -1
+    assert sh(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, 128, 4, 1, 128, 64, 0.5, FAKE, need - 1, N) == -1
+    assert sh(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, 128, 4, 1, 128, 48, 0.5, FAKE, need, N) == -2
+    assert sh(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, 128, 4, 1, 64, 64, 0.5, FAKE, need, N) == -2
+    # the dense share needs no pooled keys and no workspace
+    assert lib.sol_attn_shard_workspace_size(256, 128, 0, 1, 128, 64, -math.inf) == 0
+    cp = lib.sol_attn_combine_partials
+    assert cp(FAKE, FAKE, 0, FAKE, N, 64, 1, 128, N) == -1      # S = 0
+    assert cp(FAKE, N, 2, FAKE, N, 64, 1, 128, N) == -1
+    assert cp(FAKE, FAKE, 2, FAKE, N, 64, 1, 96, N) == -2
 
 
 def test_workspace_sizes(lib):
