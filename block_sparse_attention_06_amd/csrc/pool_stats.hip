@@ -239,11 +239,16 @@ __global__ __launch_bounds__(256) void moments_kernel(MomentArgs a) {
   }
   const float inv_nb = 1.f / (float)a.nb;
   const float mr = sr * inv_nb;
+  // Stored form: the 32 x 32 blocks of C above the diagonal doubled, those
+  // below it zero -- the same quadratic form q^T C q (C is symmetric), with
+  // 10 of the 16 blocks left to multiply.  Doubling is exact in both parts.
+  const int rbk = r >> 5, cbk = c0 >> 5;
+  const float wblk = cbk > rbk ? 2.f : (cbk == rbk ? 1.f : 0.f);
   bf16x8 hi, lo;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     __bf16 hh, ll;
-    split_bf16(__builtin_fmaf(-mr, sc[k] * inv_nb, acc[k] * inv_nb), hh, ll);
+    split_bf16(wblk * __builtin_fmaf(-mr, sc[k] * inv_nb, acc[k] * inv_nb), hh, ll);
     hi[k] = hh;
     lo[k] = ll;
   }
@@ -265,13 +270,16 @@ hipError_t launch_moments(const MomentArgs& a, hipStream_t s) {
 // stats_moment_kernel: one wave per 32 query rows, four per 128-row tile, and
 // kMomentTiles consecutive tiles per workgroup, so that C (hi and lo, 64 KiB)
 // is staged in LDS once per 1024 rows (16-byte chunk c of row R at
-// c ^ (R % 16)).  Y^T = C Q^T runs on MFMA as 4 row tiles x 8 k-steps x (hi,
-// lo); each lane dots its 64 accumulator elements with the matching query
-// values, which it already holds as MFMA operands, and adds the partner lane's
-// half.  The next tile's query fragment is loaded while this one's products run.
+// c ^ (R % 16)).  Y^T = C Q^T runs on MFMA over the stored block-triangular C:
+// row tile ct takes the k-steps of column blocks ct .. 3 only (20 of 32
+// k-steps, x (hi, lo)); each lane dots the accumulator elements of a row tile
+// with the matching query values, which it already holds as MFMA operands,
+// and adds the partner lane's half.  A wave takes two query tiles per pass, so
+// each C operand read from LDS feeds two products; the next pair's query
+// fragments load while this pair's products run.
 constexpr int kMomentTiles = 8;
 
-__global__ __launch_bounds__(256) void stats_moment_kernel(StatsMomentArgs a) {
+__global__ __launch_bounds__(256, 2) void stats_moment_kernel(StatsMomentArgs a) {
   __shared__ __attribute__((aligned(16))) u16 chs[kHeadDim * kHeadDim];
   __shared__ __attribute__((aligned(16))) u16 cls[kHeadDim * kHeadDim];
   __shared__ float mb[kHeadDim];
@@ -279,7 +287,8 @@ __global__ __launch_bounds__(256) void stats_moment_kernel(StatsMomentArgs a) {
   const int h = blockIdx.y;
   const u16* ch = a.chi + (int64_t)h * kHeadDim * kHeadDim;
   const u16* cl = a.clo + (int64_t)h * kHeadDim * kHeadDim;
-  for (int e = tid; e < kHeadDim * 16; e += 256) {
+#pragma unroll
+  for (int e = tid; e < kHeadDim * 16; e += 256) {  // all loads in flight at once
     const int R = e >> 4, c = e & 15;
     const u32x4 xh = gload<u32x4>(ch + R * kHeadDim + c * 8);
     const u32x4 xl = gload<u32x4>(cl + R * kHeadDim + c * 8);
@@ -290,49 +299,66 @@ __global__ __launch_bounds__(256) void stats_moment_kernel(StatsMomentArgs a) {
   if (tid < kHeadDim) mb[tid] = a.mbar[(int64_t)h * kHeadDim + tid];
   const u16* qh = a.q + (int64_t)h * a.N * kHeadDim;
   const int row0 = blockIdx.x * kMomentTiles * kQTile + wave * 32 + (lane & 31);
-  QFrag qf;
-  load_qfrag(qf, qh, row0, row0 < a.N, g);
+  QFrag qa, qb;
+  load_qfrag(qa, qh, row0, row0 < a.N, g);
+  load_qfrag(qb, qh, row0 + kQTile, row0 + kQTile < a.N, g);
   __syncthreads();
   const int r = lane & 31;
-  for (int t = 0; t < kMomentTiles; ++t) {
-    const int row = row0 + t * kQTile;
-    if (row - (lane & 31) >= a.N) break;  // wave-uniform: the wave's first row is past the end
-    const bool valid = row < a.N;
-    QFrag qn;
-    const int rown = row + kQTile;
-    if (t + 1 < kMomentTiles) load_qfrag(qn, qh, rown, rown < a.N, g);
-    f32x16 y[4];
+  const float scale = 0.08838834764831845f;  // 1/sqrt(128)
+  for (int t = 0; t < kMomentTiles; t += 2) {
+    const int rowa = row0 + t * kQTile, rowb = rowa + kQTile;
+    if (rowa - r >= a.N) break;  // wave-uniform: the wave's first row is past the end
+    QFrag na, nb;
+    if (t + 2 < kMomentTiles) {
+      load_qfrag(na, qh, rowa + 2 * kQTile, rowa + 2 * kQTile < a.N, g);
+      load_qfrag(nb, qh, rowb + 2 * kQTile, rowb + 2 * kQTile < a.N, g);
+    }
+    float s2a = 0.f, s2b = 0.f;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      y[ct] = f32x16{};
+      f32x16 ya = {}, yb = {};
       const int R = ct * 32 + r;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
+      for (int ks = 2 * ct; ks < 8; ++ks) {
         const int off = R * kHeadDim + (((ks * 2 + g) ^ (R & 15)) << 3);
         const bf16x8 hi = *reinterpret_cast<const bf16x8*>(&chs[off]);
         const bf16x8 lo = *reinterpret_cast<const bf16x8*>(&cls[off]);
-        y[ct] = mfma32(hi, qf.k[ks], y[ct]);
-        y[ct] = mfma32(lo, qf.k[ks], y[ct]);
+        ya = mfma32(hi, qa.k[ks], ya);
+        yb = mfma32(hi, qb.k[ks], yb);
+        ya = mfma32(lo, qa.k[ks], ya);
+        yb = mfma32(lo, qb.k[ks], yb);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        s2a = __builtin_fmaf(ya[e], (float)qa.k[2 * ct + (e >> 3)][e & 7], s2a);
+        s2b = __builtin_fmaf(yb[e], (float)qb.k[2 * ct + (e >> 3)][e & 7], s2b);
       }
     }
-    float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        s2 = __builtin_fmaf(y[ct][e], (float)qf.k[2 * ct + (e >> 3)][e & 7], s2);
+    float s1a = 0.f, s1b = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) s1 = __builtin_fmaf((float)qf.k[ks][k], mb[16 * ks + 8 * g + k], s1);
-    s1 += __shfl_xor(s1, 32);
-    s2 += __shfl_xor(s2, 32);
-    if (g == 0 && valid) {
-      const float scale = 0.08838834764831845f;  // 1/sqrt(128)
-      a.mu[(int64_t)h * a.N + row] = s1 * scale;
-      a.sigma[(int64_t)h * a.N + row] = sqrtf(fmaxf(s2, 0.f)) * scale;
+      for (int k = 0; k < 8; ++k) {
+        const float m = mb[16 * ks + 8 * g + k];
+        s1a = __builtin_fmaf((float)qa.k[ks][k], m, s1a);
+        s1b = __builtin_fmaf((float)qb.k[ks][k], m, s1b);
+      }
+    s1a += __shfl_xor(s1a, 32);
+    s2a += __shfl_xor(s2a, 32);
+    s1b += __shfl_xor(s1b, 32);
+    s2b += __shfl_xor(s2b, 32);
+    if (g == 0 && rowa < a.N) {
+      a.mu[(int64_t)h * a.N + rowa] = s1a * scale;
+      a.sigma[(int64_t)h * a.N + rowa] = sqrtf(fmaxf(s2a, 0.f)) * scale;
     }
-    if (t + 1 < kMomentTiles) qf = qn;
+    if (g == 0 && rowb < a.N) {
+      a.mu[(int64_t)h * a.N + rowb] = s1b * scale;
+      a.sigma[(int64_t)h * a.N + rowb] = sqrtf(fmaxf(s2b, 0.f)) * scale;
+    }
+    if (t + 2 < kMomentTiles) {
+      qa = na;
+      qb = nb;
+    }
   }
 }
 
