@@ -66,13 +66,14 @@ def _check_sampled(name, beta, heads):
         check_close(go[h][rows], ro, gl[h][rows], rl, what=f"{name} beta {beta} h{h}")
 
 
-@pytest.mark.parametrize("beta", [float("-inf"), 0.0, 0.5])
+@pytest.mark.parametrize("beta", [float("-inf"), 0.0, 0.5, 1.0])
 def test_stage1(beta):
     _check_sampled("stage1", beta, heads=(0, 13, 31))
 
 
-def test_stage2():
-    _check_sampled("stage2", 0.5, heads=(0, 31))
+@pytest.mark.parametrize("beta", [0.0, 0.5, 1.0])
+def test_stage2(beta):
+    _check_sampled("stage2", beta, heads=(0, 31))
 
 
 @pytest.mark.parametrize("beta", [0.5, 1.0])
