@@ -137,6 +137,47 @@ def fp8_projection(sa, torch, tokens, hidden, dev, stream, reps=5):
             "pct_fp8_peak": 100 * flops / g_ms / 1e9 / PEAK_FP8_TFLOPS}
 
 
+def workload_lines(sa, torch, name, to_dev, stream, reps=5):
+    """ms/call, dense-equivalent TFLOP/s and achieved densities of one of the
+    smaller latent workloads (same clustered generator), per beta."""
+    from synth import WORKLOADS, clustered
+    w = WORKLOADS[name]
+    H, N, d, B = w.heads, w.n, w.head_dim, w.block
+    Q, K, V = clustered(w, threads=16)
+    q, k, v = to_dev(Q), to_dev(K), to_dev(V)
+    out = torch.empty_like(q)
+    lse = torch.empty((H, N), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(1, sa.sol_attn_workspace_size(N, N, H, d, B, sa.SOL_SPARSE)),
+                     dtype=torch.uint8, device=q.device)
+    kb, _ = sa.sol_attn_pool(k, v, B)
+    mu, sigma = sa.sol_attn_row_stats(q, kb, B, N)
+    nb = (N + B - 1) // B
+    flops = 4.0 * H * N * N * d
+    res = {"heads": H, "tokens": N, "block": B, "centres": w.centres, "seed": w.seed}
+    for beta in w.betas:
+        mode = sa.SOL_DENSE if beta == float("-inf") else sa.SOL_SPARSE
+        call = lambda: sa.sol_attn_forward(q, k, v, B=B, beta=beta, mode=mode, workspace=ws,
+                                           out=out, lse=lse)
+        call()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            call()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        line = {"ms_per_call": ms, "dense_equiv_tflops": flops / ms / 1e9}
+        if mode == sa.SOL_SPARSE:
+            _, c = sa.sol_attn_block_mask(q, kb, mu, sigma, beta, B, N, want_mask=False)
+            c = c.cpu().numpy()
+            line.update(rho_row=c[0] / (H * N * nb), rho_tile32=c[1] / (H * ((N + 31) // 32) * nb),
+                        rho_tile128=c[2] / c[3])
+        res["beta_" + ("-inf" if beta == float("-inf") else str(beta))] = line
+    del q, k, v, out, ws
+    return res
+
+
 def kv_sharded(sa, torch, q, k, v, B, beta, stream, dense_flops, unsplit_ms, ranks=2, reps=3):
     """Key-sharded Sol-Attn at 4K on one GPU: each rank's share of whole key
     blocks (its keys against every query, thresholds from the pooled keys of
@@ -386,6 +427,9 @@ def main():
         extras["4k_sparse_kv_sharded"] = kv_sharded(sa, torch, q, k, v, B, args.beta, stream,
                                                     dense_flops, call_ms)
         extras["fp8_projection_4k"] = fp8_projection(sa, torch, N, H * d, q.device, stream)
+        log("stage-1 and stage-2 workloads")
+        extras["stage1_768x512"] = workload_lines(sa, torch, "stage1", to_dev, stream)
+        extras["stage2_1536x1024"] = workload_lines(sa, torch, "stage2", to_dev, stream)
         extras["na3d_decoder_tile_4k"] = na3d_decoder_tile(sa, torch, q.device, stream)
 
     cpu = None
