@@ -353,7 +353,8 @@ def main():
     nrep = max(3, args.steps)
     e = [torch.cuda.Event(enable_timing=True) for _ in range(3 * nrep)]
     moment = (N + B - 1) // B >= 128
-    mws = torch.empty(H * (2 * 128 * 128 * 2 + 128 * 4), dtype=torch.uint8, device=q.device)
+    mws = torch.empty(H * (2 * 128 * 128 * 2 + 128 * 4 + 8 * (128 * 128 + 2 * 128) * 4),
+                      dtype=torch.uint8, device=q.device)
     for i in range(nrep):
         e[3 * i].record(stream)
         kb_, vb_ = sa.sol_attn_pool(k, v, B)

@@ -161,12 +161,13 @@ def sol_attn_row_stats_moment(q: torch.Tensor, kbar: torch.Tensor, B: int, Nk: i
                               workspace: Optional[torch.Tensor] = None, stream=None):
     """``(mu, sigma)`` as :func:`sol_attn_row_stats`, in moment form (the form the
     forward pass uses from 128 key blocks on).  ``workspace`` (uint8, at least
-    ``H * (2*128*128*2 + 128*4)`` bytes) is allocated when not given."""
+    ``H * (2*128*128*2 + 128*4 + 8*(128*128 + 2*128)*4)`` bytes) is allocated
+    when not given."""
     lib = load_library()
     _want(q, "q", torch.bfloat16, 3)
     _want(kbar, "kbar", torch.float32, 3)
     H, N, d = q.shape
-    need = H * (2 * d * d * 2 + d * 4)
+    need = H * (2 * d * d * 2 + d * 4 + 8 * (d * d + 2 * d) * 4)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     mu = torch.empty((H, N), dtype=torch.float32, device=q.device)

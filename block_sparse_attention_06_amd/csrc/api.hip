@@ -17,7 +17,8 @@ constexpr int kSplitTarget = 4 * kCUs;  // workgroups wanted before splitting ke
 // From this many key blocks on, the row statistics use the moment form (2 d^2
 // multiply-adds per row instead of 2 d nb).
 constexpr int kMomentMinBlocks = 128;
-constexpr size_t kMomentBytesPerHead = 2 * 128 * 128 * sizeof(uint16_t) + 128 * sizeof(float);
+constexpr size_t kMomentBytesPerHead = 2 * 128 * 128 * sizeof(uint16_t) + 128 * sizeof(float) +
+                                       (size_t)kMomentSplits * kMomentPartFloats * sizeof(float);
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -52,7 +53,7 @@ struct Plan {
   Split sp, dn;  // sparse plan (blocks of B) and dense plan (tiles of 128 keys)
   int max_splits;
   size_t off_kbar, off_vbar, off_vsum, off_khi, off_klo, off_mu, off_sigma, off_po, off_pml, bytes;
-  size_t off_chi, off_clo, off_mbar;  // moment-form statistics (nb >= kMomentMinBlocks)
+  size_t off_chi, off_clo, off_mbar, off_mpart;  // moment-form statistics (nb >= kMomentMinBlocks)
   bool moments;
 };
 
@@ -87,6 +88,7 @@ Plan make_plan(int N, int Nk, int H, int B, int mode) {
       p.off_chi = take((size_t)H * 128 * 128 * sizeof(uint16_t));
       p.off_clo = take((size_t)H * 128 * 128 * sizeof(uint16_t));
       p.off_mbar = take((size_t)H * 128 * sizeof(float));
+    p.off_mpart = take((size_t)H * kMomentSplits * kMomentPartFloats * sizeof(float));
     }
   }
   if (p.max_splits > 1) {
@@ -104,7 +106,7 @@ Plan make_plan(int N, int Nk, int H, int B, int mode) {
 struct ShardPlan {
   int nb, nb_pad;
   size_t off_kbar, off_vbar, off_vsum, off_khi, off_klo, off_mu, off_sigma;
-  size_t off_chi, off_clo, off_mbar, bytes;
+  size_t off_chi, off_clo, off_mbar, off_mpart, bytes;
   bool moments;
 };
 
@@ -132,6 +134,7 @@ ShardPlan make_shard_plan(int N, int Nk, int nb_all, int H, int B, bool sparse) 
     p.off_chi = take((size_t)H * 128 * 128 * sizeof(uint16_t));
     p.off_clo = take((size_t)H * 128 * 128 * sizeof(uint16_t));
     p.off_mbar = take((size_t)H * 128 * sizeof(float));
+    p.off_mpart = take((size_t)H * kMomentSplits * kMomentPartFloats * sizeof(float));
   }
   p.bytes = off;
   return p;
@@ -195,8 +198,9 @@ int sol_attn_row_stats_moment(const uint16_t* q, const float* kbar, float* mu, f
   if (!aligned(q, 16) || !aligned(kbar, 16) || !aligned(workspace, 256)) return SOL_ERR_INVALID_ARG;
   if (ws_bytes < (size_t)H * kMomentBytesPerHead) return SOL_ERR_INVALID_ARG;
   char* ws = (char*)workspace;
-  MomentArgs ma{kbar, (uint16_t*)ws, (uint16_t*)(ws + (size_t)H * 128 * 128 * sizeof(uint16_t)),
-                (float*)(ws + (size_t)H * 2 * 128 * 128 * sizeof(uint16_t)), H, cdiv(Nk, B)};
+  const size_t c_bytes = (size_t)H * 128 * 128 * sizeof(uint16_t);
+  MomentArgs ma{kbar, (uint16_t*)ws, (uint16_t*)(ws + c_bytes), (float*)(ws + 2 * c_bytes),
+                (float*)(ws + 2 * c_bytes + (size_t)H * 128 * sizeof(float)), H, cdiv(Nk, B)};
   if (int r = hip_status(launch_moments(ma, (hipStream_t)stream))) return r;
   StatsMomentArgs sm{q, ma.chi, ma.clo, ma.mbar, mu, sigma, N, H};
   return hip_status(launch_stats_moment(sm, (hipStream_t)stream));
@@ -284,7 +288,7 @@ int sol_attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, ui
     float* sigma = (float*)(ws + p.off_sigma);
     if (p.moments) {
       MomentArgs ma{pa.kbar, (uint16_t*)(ws + p.off_chi), (uint16_t*)(ws + p.off_clo),
-                    (float*)(ws + p.off_mbar), H, sp.nb};
+                    (float*)(ws + p.off_mbar), (float*)(ws + p.off_mpart), H, sp.nb};
       if (int r = hip_status(launch_moments(ma, s))) return r;
       StatsMomentArgs sm{q, ma.chi, ma.clo, ma.mbar, mu, sigma, N, H};
       if (int r = hip_status(launch_stats_moment(sm, s))) return r;
@@ -365,7 +369,7 @@ int sol_attn_forward_shard(const uint16_t* q, const uint16_t* k, const uint16_t*
     float* sigma = (float*)(ws + p.off_sigma);
     if (p.moments) {
       MomentArgs ma{kbar_all, (uint16_t*)(ws + p.off_chi), (uint16_t*)(ws + p.off_clo),
-                    (float*)(ws + p.off_mbar), H, nb_all};
+                    (float*)(ws + p.off_mbar), (float*)(ws + p.off_mpart), H, nb_all};
       if (int r = hip_status(launch_moments(ma, s))) return r;
       StatsMomentArgs sm{q, ma.chi, ma.clo, ma.mbar, mu, sigma, N, H};
       if (int r = hip_status(launch_stats_moment(sm, s))) return r;

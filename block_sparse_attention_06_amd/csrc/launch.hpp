@@ -27,11 +27,18 @@ struct StatsArgs {
 
 // Moment form of the row statistics: mbar = mean_j kbar_j and the covariance
 // C = mean_j (kbar_j - mbar)(kbar_j - mbar)^T of the pooled keys, per head.
+// The pooled keys are split into kMomentSplits ranges of blocks; each range's
+// shifted partial sums (128 x 128 second moment, 128 row sums, 128 column
+// sums) go to `part` before the final kernel adds them.
+constexpr int kMomentSplits = 8;
+constexpr int kMomentPartFloats = 128 * 128 + 2 * 128;
+
 struct MomentArgs {
   const float* kbar;  // [H, nb, 128]
   uint16_t* chi;      // [H, 128, 128] bf16 hi part of C, rows permuted for the MFMA A operand
   uint16_t* clo;      // [H, 128, 128] bf16 lo part
   float* mbar;        // [H, 128]
+  float* part;        // [H, kMomentSplits, kMomentPartFloats] partial sums
   int H, nb;
 };
 

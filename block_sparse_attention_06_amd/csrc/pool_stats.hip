@@ -172,16 +172,12 @@ hipError_t launch_stats(const StatsArgs& a, hipStream_t s) {
 // Same quantities as stats_kernel up to
 // rounding, at 2 d^2 instead of 2 d nb multiply-adds per row.
 //
-// moments_kernel: one workgroup per (16 rows of C, head), one pass over the
-// pooled keys.  32 keys at a time are staged in LDS, shifted by the head's
-// first pooled key (so the second moments carry no large common offset: the
-// shift-then-correct form keeps the cancellation to the keys' own spread),
-// while the next 32 are already being loaded; each thread accumulates 8
-// entries of the shifted second moment plus the shifted sums of its row and
-// columns, all in fp32.  C = S2 / nb - (S1_r / nb)(S1_c / nb); mbar = k0 + S1 / nb.
-// C is written as bf16 hi + lo parts (~16 significant bits), rows permuted
-// (see c_row_pos) so that stats_moment_kernel's accumulator elements line up
-// with its query fragment.
+// Moments of the pooled keys, in two kernels.  32 keys at a time are staged
+// in LDS, shifted by the head's first pooled key (so the second moments carry
+// no large common offset: the shift-then-correct form keeps the cancellation
+// to the keys' own spread), while the next 32 are already being loaded; each
+// thread accumulates 8 entries of the shifted second moment plus the shifted
+// sums of its row and columns, all in fp32.
 // ---------------------------------------------------------------------------
 
 // Stored position, within its 32-row tile, of row `off` of C.  The MFMA
@@ -193,36 +189,42 @@ __device__ __forceinline__ int c_row_pos(int off) {
   return 8 * (2 * (off >> 4) + ((off >> 2) & 1)) + 4 * ((off >> 3) & 1) + (off & 3);
 }
 
-__global__ __launch_bounds__(256) void moments_kernel(MomentArgs a) {
+// moments_part_kernel: workgroup (16 rows of C, block range s, head); the
+// pooled keys are split into kMomentSplits contiguous ranges so that no
+// workgroup walks all of them.  Each writes its shifted partial sums (second
+// moment, row sums, column sums); moments_final_kernel adds the ranges.
+__global__ __launch_bounds__(256) void moments_part_kernel(MomentArgs a) {
   __shared__ float kc[kChunk][kHeadDim + 4];
   __shared__ float k0s[kHeadDim];
-  const int rb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int rb = blockIdx.x, sp = blockIdx.y, h = blockIdx.z, tid = threadIdx.x;
   const float* kb = a.kbar + (int64_t)h * a.nb * kHeadDim;
   if (tid < kHeadDim) k0s[tid] = kb[tid];
+  const int per = (a.nb + kMomentSplits - 1) / kMomentSplits;
+  const int jb = min(a.nb, sp * per), je = min(a.nb, jb + per);
   constexpr int kPer = kChunk * kHeadDim / 256;  // staged values per thread
   float nxt[kPer];
   auto load = [&](int j0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = tid + 256 * i, j = j0 + (e >> 7);
-      nxt[i] = j < a.nb ? kb[(int64_t)j * kHeadDim + (e & (kHeadDim - 1))] : 0.f;
+      nxt[i] = j < je ? kb[(int64_t)j * kHeadDim + (e & (kHeadDim - 1))] : 0.f;
     }
   };
-  load(0);
+  load(jb);
   const int r = rb * 16 + (tid >> 4), c0 = (tid & 15) * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float sc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float sr = 0.f;
-  for (int j0 = 0; j0 < a.nb; j0 += kChunk) {
+  for (int j0 = jb; j0 < je; j0 += kChunk) {
     __syncthreads();  // the previous chunk has been consumed (and k0s is visible)
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = tid + 256 * i, j = j0 + (e >> 7), cc = e & (kHeadDim - 1);
-      kc[e >> 7][cc] = j < a.nb ? nxt[i] - k0s[cc] : 0.f;
+      kc[e >> 7][cc] = j < je ? nxt[i] - k0s[cc] : 0.f;
     }
     __syncthreads();
-    if (j0 + kChunk < a.nb) load(j0 + kChunk);
-    const int nj = min(kChunk, a.nb - j0);
+    if (j0 + kChunk < je) load(j0 + kChunk);
+    const int nj = min(kChunk, je - j0);
     for (int jj = 0; jj < nj; ++jj) {
       const float x = kc[jj][r];
       const f32x4 y0 = *reinterpret_cast<const f32x4*>(&kc[jj][c0]);
@@ -235,6 +237,42 @@ __global__ __launch_bounds__(256) void moments_kernel(MomentArgs a) {
         sc[k] += y0[k];
         sc[k + 4] += y1[k];
       }
+    }
+  }
+  float* part = a.part + ((int64_t)h * kMomentSplits + sp) * kMomentPartFloats;
+  *reinterpret_cast<f32x4*>(part + r * kHeadDim + c0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  *reinterpret_cast<f32x4*>(part + r * kHeadDim + c0 + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  if ((tid & 15) == 0) part[kHeadDim * kHeadDim + r] = sr;
+  if (rb == 0 && (tid >> 4) == 0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) part[kHeadDim * kHeadDim + kHeadDim + c0 + k] = sc[k];
+  }
+}
+
+// moments_final_kernel: workgroup (16 rows of C, head).  Adds the ranges'
+// partial sums, then C = S2 / nb - (S1_r / nb)(S1_c / nb), mbar = k0 + S1 / nb.
+// C is written as bf16 hi + lo parts (~16 significant bits) in its stored
+// block-triangular form, rows permuted (c_row_pos) so that
+// stats_moment_kernel's accumulator elements line up with its query fragment.
+__global__ __launch_bounds__(256) void moments_final_kernel(MomentArgs a) {
+  const int rb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int r = rb * 16 + (tid >> 4), c0 = (tid & 15) * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float sc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float sr = 0.f;
+  for (int sp = 0; sp < kMomentSplits; ++sp) {
+    const float* part = a.part + ((int64_t)h * kMomentSplits + sp) * kMomentPartFloats;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(part + r * kHeadDim + c0);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(part + r * kHeadDim + c0 + 4);
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(part + kHeadDim * kHeadDim + kHeadDim + c0);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(part + kHeadDim * kHeadDim + kHeadDim + c0 + 4);
+    sr += part[kHeadDim * kHeadDim + r];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[k] += x0[k];
+      acc[k + 4] += x1[k];
+      sc[k] += s0[k];
+      sc[k + 4] += s1[k];
     }
   }
   const float inv_nb = 1.f / (float)a.nb;
@@ -256,32 +294,44 @@ __global__ __launch_bounds__(256) void moments_kernel(MomentArgs a) {
   *reinterpret_cast<bf16x8*>(a.chi + pos) = hi;
   *reinterpret_cast<bf16x8*>(a.clo + pos) = lo;
   if (rb == 0 && (tid >> 4) == 0) {
+    const float* kb = a.kbar + (int64_t)h * a.nb * kHeadDim;
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      a.mbar[(int64_t)h * kHeadDim + c0 + k] = k0s[c0 + k] + sc[k] * inv_nb;
+    for (int k = 0; k < 8; ++k) a.mbar[(int64_t)h * kHeadDim + c0 + k] = kb[c0 + k] + sc[k] * inv_nb;
   }
 }
 
 hipError_t launch_moments(const MomentArgs& a, hipStream_t s) {
-  moments_kernel<<<dim3(kHeadDim / 16, a.H), 256, 0, s>>>(a);
+  moments_part_kernel<<<dim3(kHeadDim / 16, kMomentSplits, a.H), 256, 0, s>>>(a);
+  if (hipError_t e = hipGetLastError()) return e;
+  moments_final_kernel<<<dim3(kHeadDim / 16, a.H), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 // stats_moment_kernel: one wave per 32 query rows, four per 128-row tile, and
-// kMomentTiles consecutive tiles per workgroup, so that C (hi and lo, 64 KiB)
-// is staged in LDS once per 1024 rows (16-byte chunk c of row R at
-// c ^ (R % 16)).  Y^T = C Q^T runs on MFMA over the stored block-triangular C:
-// row tile ct takes the k-steps of column blocks ct .. 3 only (20 of 32
-// k-steps, x (hi, lo)); each lane dots the accumulator elements of a row tile
-// with the matching query values, which it already holds as MFMA operands,
-// and adds the partner lane's half.  A wave takes two query tiles per pass, so
-// each C operand read from LDS feeds two products; the next pair's query
-// fragments load while this pair's products run.
+// kMomentTiles consecutive tiles per workgroup.  Y^T = C Q^T runs on MFMA over
+// the stored block-triangular C: row tile ct takes the k-steps of column
+// blocks ct .. 3 only (20 of 32 k-steps, x (hi, lo)); each lane dots the
+// accumulator elements of a row tile with the matching query values, which it
+// already holds as MFMA operands, and adds the partner lane's half.  A wave
+// takes two query tiles per pass, so each C operand read from LDS feeds two
+// products.
+//
+// Only the used blocks of C are staged, once per workgroup: row R of tile ct
+// keeps 16-byte chunks 4 ct .. 15, at positions 0 .. 15 - 4 ct of a row of
+// kCW[ct] chunks (an odd count, so that 8 consecutive rows start on different
+// banks: conflict-free operand reads).  45 KiB per workgroup; three
+// workgroups per CU hide the query loads (there is no register prefetch).
 constexpr int kMomentTiles = 8;
+constexpr int kCW0 = 17, kCW1 = 13, kCW2 = 9, kCW3 = 5;   // padded row widths (chunks)
+constexpr int kCBase1 = 32 * kCW0, kCBase2 = kCBase1 + 32 * kCW1, kCBase3 = kCBase2 + 32 * kCW2;
+constexpr int kCChunks = kCBase3 + 32 * kCW3;             // 1408 chunks per part
 
-__global__ __launch_bounds__(256, 2) void stats_moment_kernel(StatsMomentArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 chs[kHeadDim * kHeadDim];
-  __shared__ __attribute__((aligned(16))) u16 cls[kHeadDim * kHeadDim];
+__device__ __forceinline__ int c_width(int ct) { return ct == 0 ? kCW0 : ct == 1 ? kCW1 : ct == 2 ? kCW2 : kCW3; }
+__device__ __forceinline__ int c_base(int ct) { return ct == 0 ? 0 : ct == 1 ? kCBase1 : ct == 2 ? kCBase2 : kCBase3; }
+
+__global__ __launch_bounds__(256, 3) void stats_moment_kernel(StatsMomentArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 chs[kCChunks * 8];
+  __shared__ __attribute__((aligned(16))) u16 cls[kCChunks * 8];
   __shared__ float mb[kHeadDim];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
   const int h = blockIdx.y;
@@ -289,38 +339,35 @@ __global__ __launch_bounds__(256, 2) void stats_moment_kernel(StatsMomentArgs a)
   const u16* cl = a.clo + (int64_t)h * kHeadDim * kHeadDim;
 #pragma unroll
   for (int e = tid; e < kHeadDim * 16; e += 256) {  // all loads in flight at once
-    const int R = e >> 4, c = e & 15;
-    const u32x4 xh = gload<u32x4>(ch + R * kHeadDim + c * 8);
-    const u32x4 xl = gload<u32x4>(cl + R * kHeadDim + c * 8);
-    const int off = R * kHeadDim + ((c ^ (R & 15)) << 3);
-    *reinterpret_cast<u32x4*>(&chs[off]) = xh;
-    *reinterpret_cast<u32x4*>(&cls[off]) = xl;
+    const int R = e >> 4, c = e & 15, ct = R >> 5;
+    if (c >= 4 * ct) {
+      const u32x4 xh = gload<u32x4>(ch + R * kHeadDim + c * 8);
+      const u32x4 xl = gload<u32x4>(cl + R * kHeadDim + c * 8);
+      const int off = (c_base(ct) + (R & 31) * c_width(ct) + c - 4 * ct) * 8;
+      *reinterpret_cast<u32x4*>(&chs[off]) = xh;
+      *reinterpret_cast<u32x4*>(&cls[off]) = xl;
+    }
   }
   if (tid < kHeadDim) mb[tid] = a.mbar[(int64_t)h * kHeadDim + tid];
   const u16* qh = a.q + (int64_t)h * a.N * kHeadDim;
   const int row0 = blockIdx.x * kMomentTiles * kQTile + wave * 32 + (lane & 31);
-  QFrag qa, qb;
-  load_qfrag(qa, qh, row0, row0 < a.N, g);
-  load_qfrag(qb, qh, row0 + kQTile, row0 + kQTile < a.N, g);
   __syncthreads();
   const int r = lane & 31;
   const float scale = 0.08838834764831845f;  // 1/sqrt(128)
   for (int t = 0; t < kMomentTiles; t += 2) {
     const int rowa = row0 + t * kQTile, rowb = rowa + kQTile;
     if (rowa - r >= a.N) break;  // wave-uniform: the wave's first row is past the end
-    QFrag na, nb;
-    if (t + 2 < kMomentTiles) {
-      load_qfrag(na, qh, rowa + 2 * kQTile, rowa + 2 * kQTile < a.N, g);
-      load_qfrag(nb, qh, rowb + 2 * kQTile, rowb + 2 * kQTile < a.N, g);
-    }
-    float s2a = 0.f, s2b = 0.f;
+    QFrag qa, qb;
+    load_qfrag(qa, qh, rowa, rowa < a.N, g);
+    load_qfrag(qb, qh, rowb, rowb < a.N, g);
+    float s2a = 0.f, s2b = 0.f, s1a = 0.f, s1b = 0.f;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       f32x16 ya = {}, yb = {};
-      const int R = ct * 32 + r;
+      const int rbase = (c_base(ct) + r * c_width(ct) - 4 * ct) * 8;
 #pragma unroll
       for (int ks = 2 * ct; ks < 8; ++ks) {
-        const int off = R * kHeadDim + (((ks * 2 + g) ^ (R & 15)) << 3);
+        const int off = rbase + (ks * 2 + g) * 8;
         const bf16x8 hi = *reinterpret_cast<const bf16x8*>(&chs[off]);
         const bf16x8 lo = *reinterpret_cast<const bf16x8*>(&cls[off]);
         ya = mfma32(hi, qa.k[ks], ya);
@@ -328,21 +375,19 @@ __global__ __launch_bounds__(256, 2) void stats_moment_kernel(StatsMomentArgs a)
         ya = mfma32(lo, qa.k[ks], ya);
         yb = mfma32(lo, qb.k[ks], yb);
       }
+      // element e pairs with query dimension 16 (2 ct + e / 8) + 8 g + e % 8;
+      // the same values give this tile's part of q . mbar
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        s2a = __builtin_fmaf(ya[e], (float)qa.k[2 * ct + (e >> 3)][e & 7], s2a);
-        s2b = __builtin_fmaf(yb[e], (float)qb.k[2 * ct + (e >> 3)][e & 7], s2b);
+        const int ks = 2 * ct + (e >> 3), k = e & 7;
+        const float m = mb[16 * ks + 8 * g + k];
+        const float xa = (float)qa.k[ks][k], xb = (float)qb.k[ks][k];
+        s2a = __builtin_fmaf(ya[e], xa, s2a);
+        s2b = __builtin_fmaf(yb[e], xb, s2b);
+        s1a = __builtin_fmaf(xa, m, s1a);
+        s1b = __builtin_fmaf(xb, m, s1b);
       }
     }
-    float s1a = 0.f, s1b = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float m = mb[16 * ks + 8 * g + k];
-        s1a = __builtin_fmaf((float)qa.k[ks][k], m, s1a);
-        s1b = __builtin_fmaf((float)qb.k[ks][k], m, s1b);
-      }
     s1a += __shfl_xor(s1a, 32);
     s2a += __shfl_xor(s2a, 32);
     s1b += __shfl_xor(s1b, 32);
@@ -354,10 +399,6 @@ __global__ __launch_bounds__(256, 2) void stats_moment_kernel(StatsMomentArgs a)
     if (g == 0 && rowb < a.N) {
       a.mu[(int64_t)h * a.N + rowb] = s1b * scale;
       a.sigma[(int64_t)h * a.N + rowb] = sqrtf(fmaxf(s2b, 0.f)) * scale;
-    }
-    if (t + 2 < kMomentTiles) {
-      qa = na;
-      qb = nb;
     }
   }
 }

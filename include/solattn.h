@@ -105,9 +105,10 @@ int sol_attn_row_stats(const uint16_t* q, const float* kbar, float* mu, float* s
  * Equal to sol_attn_row_stats up to rounding, at 2 d^2 instead of 2 d nb
  * multiply-adds per row.
  * Arguments as sol_attn_row_stats, plus:
- * workspace  device scratch of at least H * (2 * d * d * 2 + d * 4) bytes,
- *            256-byte aligned, caller-owned; it holds mbar and C (bf16 hi and
- *            lo parts) on return.
+ * workspace  device scratch of at least H * (2 * d * d * 2 + d * 4 +
+ *            8 * (d * d + 2 * d) * 4) bytes, 256-byte aligned, caller-owned;
+ *            on return it holds C (bf16 hi and lo parts), mbar and the partial
+ *            sums of 8 ranges of blocks, in that order.
  * ws_bytes   its size; smaller returns SOL_ERR_INVALID_ARG before any launch.
  */
 int sol_attn_row_stats_moment(const uint16_t* q, const float* kbar, float* mu, float* sigma,

@@ -80,7 +80,7 @@ def test_other_entry_points_argument_errors(lib):
     assert lib.sol_attn_pool(FAKE, FAKE, FAKE, FAKE, 64, 1, 96, 64, N) == -2
     assert lib.sol_attn_pool(FAKE, FAKE, FAKE, FAKE, 64, 1, 128, 100, N) == -2
     assert lib.sol_attn_row_stats(FAKE, N, FAKE, FAKE, 64, 64, 1, 128, 64, N) == -1
-    need = 2 * 128 * 128 * 2 + 128 * 4  # one head
+    need = 2 * 128 * 128 * 2 + 128 * 4 + 8 * (128 * 128 + 2 * 128) * 4  # one head
     rsm = lib.sol_attn_row_stats_moment
     assert rsm(FAKE, FAKE, FAKE, FAKE, 64, 64, 1, 128, 64, N, need, N) == -1      # no workspace
     assert rsm(FAKE, FAKE, FAKE, FAKE, 64, 64, 1, 128, 64, FAKE, need - 1, N) == -1  # too small
