@@ -118,3 +118,63 @@ def test_share_of_rejected_blocks_can_have_a_negative_denominator():
     den = sum(p[1][0] * np.exp(p[2][0] - M) for p in parts)
     np.testing.assert_allclose(num / den, o[0], atol=1e-12)
     np.testing.assert_allclose(M + np.log(den), l[0], atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# planted mistakes: each mutated share computation must fail a pin above
+# --------------------------------------------------------------------------
+
+
+def _mutant_share(kind, q, k, v, B, beta, share):
+    """One share's partial (out, lse) with one plausible mistake planted."""
+    nk, d = k.shape
+    nb = (nk + B - 1) // B
+    bounds = [(j * B, min(nk, (j + 1) * B)) for j in range(nb)]
+    kbar = np.stack([k[s:e].mean(0) for s, e in bounds])
+    vbar = np.stack([v[s:e].mean(0) for s, e in bounds])
+    p = q @ kbar.T / np.sqrt(d)
+    in_share = np.zeros(nb, bool)
+    in_share[share] = True
+    ps = p[:, in_share] if kind == "stats_from_share" else p
+    mu, sigma = ps.mean(1), ps.std(1)
+    sel = p >= (mu + beta * sigma)[:, None]
+    s = q @ k.T / np.sqrt(d)
+    num = np.zeros((q.shape[0], d))
+    den = np.zeros(q.shape[0])
+    for j, (b0, b1) in enumerate(bounds):
+        exact_here = in_share[j] or kind == "exact_all_blocks"
+        taylor_here = in_share[j] or kind == "taylor_all_blocks"
+        e = np.exp(s[:, b0:b1]) * (sel[:, j:j + 1] & exact_here)
+        num += e @ v[b0:b1]
+        den += e.sum(1)
+        w = np.where(sel[:, j] | (not taylor_here), 0.0,
+                     (b1 - b0) * np.exp(mu) * (1 + p[:, j] - mu))
+        num += w[:, None] * vbar[j]
+        den += w
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return num / den[:, None], np.where(den > 0, np.log(np.where(den > 0, den, 1.0)), np.nan)
+
+
+@pytest.mark.parametrize("kind", ["taylor_all_blocks", "stats_from_share", "exact_all_blocks"])
+def test_planted_share_mistakes_are_caught(rng, kind):
+    q, k, v = _rand(rng, 6, 8, 1.5), _rand(rng, 45, 8, 1.5), _rand(rng, 45, 8)
+    failures = 0
+    for beta in (0.0, 0.5):
+        for share in ([0, 1], [2, 3, 4, 5]):
+            o, l = _mutant_share(kind, q, k, v, 8, beta, share)
+            bo, bl = _brute_share(q.tolist(), k.tolist(), v.tolist(), 8, beta, share)
+            ok = np.isfinite(bl) & np.isfinite(l)
+            failures += not (np.allclose(o[ok], bo[ok], atol=1e-10) and
+                             np.allclose(l[ok], bl[ok], atol=1e-10) and
+                             np.array_equal(np.isfinite(l), np.isfinite(bl)))
+    assert failures > 0, f"planted mistake {kind!r} passed every pin"
+
+
+def test_unmutated_share_copy_passes(rng):
+    q, k, v = _rand(rng, 6, 8, 1.5), _rand(rng, 45, 8, 1.5), _rand(rng, 45, 8)
+    for share in ([0, 1], [2, 3, 4, 5]):
+        o, l = _mutant_share("none", q, k, v, 8, 0.5, share)
+        ro, rl, _ = O.sol_attn_head_ref(q, k, v, 8, 0.5, blocks=share)
+        ok = np.isfinite(rl)
+        np.testing.assert_allclose(o[ok], ro[ok], atol=1e-10)
+        np.testing.assert_allclose(l[ok], rl[ok], atol=1e-10)
