@@ -28,8 +28,10 @@ struct StatsArgs {
 // Moment form of the row statistics: mbar = mean_j kbar_j and the covariance
 // C = mean_j (kbar_j - mbar)(kbar_j - mbar)^T of the pooled keys, per head.
 // The pooled keys are split into kMomentSplits ranges of blocks; each range's
-// shifted partial sums (128 x 128 second moment, 128 row sums, 128 column
-// sums) go to `part` before the final kernel adds them.
+// shifted partial sums (128 x 128 second moment, only its blocks on or above
+// the diagonal written; 128 row sums, which are also the column sums) go to
+// `part` before the final kernel adds them.  The last 128 floats of a range's
+// slot are spare.
 constexpr int kMomentSplits = 8;
 constexpr int kMomentPartFloats = 128 * 128 + 2 * 128;
 

@@ -189,63 +189,73 @@ __device__ __forceinline__ int c_row_pos(int off) {
   return 8 * (2 * (off >> 4) + ((off >> 2) & 1)) + 4 * ((off >> 3) & 1) + (off & 3);
 }
 
-// moments_part_kernel: workgroup (16 rows of C, block range s, head); the
+// moments_part_kernel: workgroup (32 rows of C, block range s, head); the
 // pooled keys are split into kMomentSplits contiguous ranges so that no
-// workgroup walks all of them.  Each writes its shifted partial sums (second
-// moment, row sums, column sums); moments_final_kernel adds the ranges.
+// workgroup walks all of them.  Wave w owns column block w (32 columns) and
+// works only at or right of the diagonal block: the blocks below it are not
+// part of the stored form of C.  A lane keeps a 4 x 4 tile and reads one
+// 16-byte row operand and one column operand per pooled key.  Each workgroup
+// writes its shifted partial sums (second moment over its blocks, sums of its
+// 32 rows); moments_final_kernel adds the ranges.  The row sums double as the
+// column sums (the same vector of shifted pooled keys summed).
 __global__ __launch_bounds__(256) void moments_part_kernel(MomentArgs a) {
-  __shared__ float kc[kChunk][kHeadDim + 4];
-  __shared__ float k0s[kHeadDim];
-  const int rb = blockIdx.x, sp = blockIdx.y, h = blockIdx.z, tid = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) float kc[kChunk][kHeadDim + 4];
+  __shared__ __attribute__((aligned(16))) float k0s[kHeadDim];
+  const int rb = blockIdx.x, sp = blockIdx.y, h = blockIdx.z, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float* kb = a.kbar + (int64_t)h * a.nb * kHeadDim;
   if (tid < kHeadDim) k0s[tid] = kb[tid];
   const int per = (a.nb + kMomentSplits - 1) / kMomentSplits;
   const int jb = min(a.nb, sp * per), je = min(a.nb, jb + per);
-  constexpr int kPer = kChunk * kHeadDim / 256;  // staged values per thread
-  float nxt[kPer];
+  constexpr int kPer = kChunk * kHeadDim / 4 / 256;  // staged 16-byte values per thread
+  f32x4 nxt[kPer];
   auto load = [&](int j0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int e = tid + 256 * i, j = j0 + (e >> 7);
-      nxt[i] = j < je ? kb[(int64_t)j * kHeadDim + (e & (kHeadDim - 1))] : 0.f;
+      const int e = tid + 256 * i, j = j0 + (e >> 5);
+      nxt[i] = j < je ? *reinterpret_cast<const f32x4*>(kb + (int64_t)j * kHeadDim + (e & 31) * 4)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
   load(jb);
-  const int r = rb * 16 + (tid >> 4), c0 = (tid & 15) * 8;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float sc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float sr = 0.f;
+  const bool active = wave >= rb;  // wave-uniform
+  const int r0 = rb * 32 + (lane >> 3) * 4, c0 = wave * 32 + (lane & 7) * 4;
+  float acc[4][4] = {};
+  float sr[4] = {0.f, 0.f, 0.f, 0.f};
   for (int j0 = jb; j0 < je; j0 += kChunk) {
     __syncthreads();  // the previous chunk has been consumed (and k0s is visible)
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int e = tid + 256 * i, j = j0 + (e >> 7), cc = e & (kHeadDim - 1);
-      kc[e >> 7][cc] = j < je ? nxt[i] - k0s[cc] : 0.f;
+      const int e = tid + 256 * i, jj = e >> 5, cc = (e & 31) * 4;
+      const f32x4 k0 = *reinterpret_cast<const f32x4*>(&k0s[cc]);
+      const f32x4 x = j0 + jj < je ? nxt[i] - k0 : f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(&kc[jj][cc]) = x;
     }
     __syncthreads();
     if (j0 + kChunk < je) load(j0 + kChunk);
-    const int nj = min(kChunk, je - j0);
-    for (int jj = 0; jj < nj; ++jj) {
-      const float x = kc[jj][r];
-      const f32x4 y0 = *reinterpret_cast<const f32x4*>(&kc[jj][c0]);
-      const f32x4 y1 = *reinterpret_cast<const f32x4*>(&kc[jj][c0 + 4]);
-      sr += x;
+    if (active) {
+      const int nj = min(kChunk, je - j0);
+      for (int jj = 0; jj < nj; ++jj) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&kc[jj][r0]);
+        const f32x4 y = *reinterpret_cast<const f32x4*>(&kc[jj][c0]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        acc[k] = __builtin_fmaf(x, y0[k], acc[k]);
-        acc[k + 4] = __builtin_fmaf(x, y1[k], acc[k + 4]);
-        sc[k] += y0[k];
-        sc[k + 4] += y1[k];
+        for (int i = 0; i < 4; ++i) {
+          sr[i] += x[i];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc[i][k] = __builtin_fmaf(x[i], y[k], acc[i][k]);
+        }
       }
     }
   }
   float* part = a.part + ((int64_t)h * kMomentSplits + sp) * kMomentPartFloats;
-  *reinterpret_cast<f32x4*>(part + r * kHeadDim + c0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-  *reinterpret_cast<f32x4*>(part + r * kHeadDim + c0 + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-  if ((tid & 15) == 0) part[kHeadDim * kHeadDim + r] = sr;
-  if (rb == 0 && (tid >> 4) == 0) {
+  if (active) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) part[kHeadDim * kHeadDim + kHeadDim + c0 + k] = sc[k];
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<f32x4*>(part + (r0 + i) * kHeadDim + c0) = f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+  }
+  if (wave == 3 && (lane & 7) == 0) {  // wave 3 is active for every row block
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[kHeadDim * kHeadDim + r0 + i] = sr[i];
   }
 }
 
@@ -257,36 +267,43 @@ __global__ __launch_bounds__(256) void moments_part_kernel(MomentArgs a) {
 __global__ __launch_bounds__(256) void moments_final_kernel(MomentArgs a) {
   const int rb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int r = rb * 16 + (tid >> 4), c0 = (tid & 15) * 8;
+  // Stored form: the 32 x 32 blocks of C above the diagonal doubled, those
+  // below it zero -- the same quadratic form q^T C q (C is symmetric), with
+  // 10 of the 16 blocks left to multiply.  Doubling is exact in both parts.
+  const int rbk = r >> 5, cbk = c0 >> 5;
+  const bool used = cbk >= rbk;  // blocks below the diagonal have no partial sums
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float sc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float sr = 0.f;
   for (int sp = 0; sp < kMomentSplits; ++sp) {
     const float* part = a.part + ((int64_t)h * kMomentSplits + sp) * kMomentPartFloats;
-    const f32x4 x0 = *reinterpret_cast<const f32x4*>(part + r * kHeadDim + c0);
-    const f32x4 x1 = *reinterpret_cast<const f32x4*>(part + r * kHeadDim + c0 + 4);
-    const f32x4 s0 = *reinterpret_cast<const f32x4*>(part + kHeadDim * kHeadDim + kHeadDim + c0);
-    const f32x4 s1 = *reinterpret_cast<const f32x4*>(part + kHeadDim * kHeadDim + kHeadDim + c0 + 4);
-    sr += part[kHeadDim * kHeadDim + r];
+    const float* sums = part + kHeadDim * kHeadDim;  // row sums (= column sums)
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(sums + c0);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(sums + c0 + 4);
+    sr += sums[r];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      acc[k] += x0[k];
-      acc[k + 4] += x1[k];
       sc[k] += s0[k];
       sc[k + 4] += s1[k];
+    }
+    if (used) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(part + r * kHeadDim + c0);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(part + r * kHeadDim + c0 + 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[k] += x0[k];
+        acc[k + 4] += x1[k];
+      }
     }
   }
   const float inv_nb = 1.f / (float)a.nb;
   const float mr = sr * inv_nb;
-  // Stored form: the 32 x 32 blocks of C above the diagonal doubled, those
-  // below it zero -- the same quadratic form q^T C q (C is symmetric), with
-  // 10 of the 16 blocks left to multiply.  Doubling is exact in both parts.
-  const int rbk = r >> 5, cbk = c0 >> 5;
   const float wblk = cbk > rbk ? 2.f : (cbk == rbk ? 1.f : 0.f);
   bf16x8 hi, lo;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    __bf16 hh, ll;
-    split_bf16(wblk * __builtin_fmaf(-mr, sc[k] * inv_nb, acc[k] * inv_nb), hh, ll);
+    __bf16 hh = (__bf16)0.f, ll = (__bf16)0.f;
+    if (used) split_bf16(wblk * __builtin_fmaf(-mr, sc[k] * inv_nb, acc[k] * inv_nb), hh, ll);
     hi[k] = hh;
     lo[k] = ll;
   }
@@ -301,7 +318,7 @@ __global__ __launch_bounds__(256) void moments_final_kernel(MomentArgs a) {
 }
 
 hipError_t launch_moments(const MomentArgs& a, hipStream_t s) {
-  moments_part_kernel<<<dim3(kHeadDim / 16, kMomentSplits, a.H), 256, 0, s>>>(a);
+  moments_part_kernel<<<dim3(kHeadDim / 32, kMomentSplits, a.H), 256, 0, s>>>(a);
   if (hipError_t e = hipGetLastError()) return e;
   moments_final_kernel<<<dim3(kHeadDim / 16, a.H), 256, 0, s>>>(a);
   return hipGetLastError();
