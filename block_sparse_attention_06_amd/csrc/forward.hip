@@ -40,6 +40,7 @@ constexpr int kRing = 5;                // LDS stages (80 KiB: two workgroups pe
 constexpr int kAhead = kRing - 1;       // units in flight beyond the one whose PV runs
 constexpr int kDmaPerUnit = 4;          // loads per wave per unit: 2 groups of 4 rows, K and V
 constexpr float kSlack = 8.f;           // log2 units the reference may lag the row max
+constexpr float kSlackSum = 256.f;      // 2^kSlack: bound on a lane's row sum of one unit
 constexpr int kLgkm0 = 0xC07F;          // s_waitcnt lgkmcnt(0)
 
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(n) alone.
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   // forms the probabilities as the bf16 B operand of the PV product (keys
   // permuted within 16 as the accumulator layout holds them) and adds their
   // row sums to l.
-  auto softmax_head = [&](f32x16& s, int key0, bool mine) __attribute__((always_inline)) {
+  auto mask_ragged = [&](f32x16& s, int key0) __attribute__((always_inline)) {
     if (key0 + kU > Nk) {  // ragged last unit: keys past the end do not exist
       // element i holds key offset acc_row(i, 0) + 4g: compare the one
       // per-lane term with scalar limits (no per-element lane offsets kept live)
@@ -212,13 +213,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       for (int i = 0; i < 16; ++i)
         if (g4 >= lim - acc_row(i, 0)) s[i] = -__builtin_inff();
     }
+  };
+  auto softmax_head = [&](f32x16& s, int key0, bool mine, float slack) __attribute__((always_inline)) {
+    mask_ragged(s, key0);
     float mx = s[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
     mx = fmaxf(mx, partner_f(mx, g));
     const float mc = mx * sl2;
     // move the reference only when the max outruns it by more than the slack
-    const bool up = mine && (mc > m + kSlack);
+    const bool up = mine && (mc > m + slack);
     if (__ballot(up)) {
       const float alpha = up ? fast_exp2(m - mc) : 1.f;
       l *= alpha;
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     if (up) m = mc;
     return mine ? -m : -__builtin_inff();
   };
-  auto softmax_tail = [&](const f32x16& s, float neg_ref, bf16x8 (&pb)[2]) __attribute__((always_inline)) {
+  auto softmax_tail = [&](const f32x16& s, float neg_ref, bf16x8 (&pb)[2]) __attribute__((always_inline)) -> float {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       pb[i >> 3][i & 7] = (__bf16)fast_exp2(__builtin_fmaf(s[i], sl2, neg_ref));
@@ -244,14 +248,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       rs0 = __builtin_amdgcn_fdot2_f32_bf16(p0, one2, rs0, false);
       rs1 = __builtin_amdgcn_fdot2_f32_bf16(p1, one2, rs1, false);
     }
-    l += rs0 + rs1;
+    return rs0 + rs1;
   };
 
   // ---- the softmax tail of one unit interleaved with the S products of the
   // next: product k, then the probabilities of elements 2k and 2k+1 (scale,
   // exponential, bf16 pair, pair row sum), fenced so that the compiler keeps
   // the order; K operand reads run four products ahead.
-  auto tail_and_s = [&](const f32x16& s_in, float neg_ref, bf16x8 (&pb)[2], int st) __attribute__((always_inline)) {
+  auto tail_and_s = [&](const f32x16& s_in, float neg_ref, bf16x8 (&pb)[2], int st, float& rsum) __attribute__((always_inline)) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
     auto kaddr = [&](int ks) __attribute__((always_inline)) {
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       rs[k >> 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rs[k >> 2], false);
       __builtin_amdgcn_sched_barrier(0);
     }
-    l += rs[0] + rs[1];
+    rsum = rs[0] + rs[1];
     return s;
   };
 
@@ -332,8 +336,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     const int st2 = st1 == kRing - 1 ? 0 : st1 + 1;
     const bool pv = (qneed & 2u) != 0, do_s = (qneed & 4u) != 0;
     bf16x8 pb[2];
-    float neg_ref = 0.f;
-    if (pv) neg_ref = softmax_head(s_in, qkey[1], (qmine & 2u) != 0);
+    float neg_ref = 0.f, rsum = 0.f;
+    const bool mine1 = (qmine & 2u) != 0;
+    if constexpr (SPARSE) {
+      // The reference starts at mu (finite) and is checked after the fact: the
+      // probabilities are formed against it and the unit goes on only if every
+      // lane's row sum stays within 2^kSlack (which bounds each probability).
+      if (pv) {
+        mask_ragged(s_in, qkey[1]);
+        neg_ref = mine1 ? -m : -__builtin_inff();
+      }
+    } else {
+      if (pv) neg_ref = softmax_head(s_in, qkey[1], mine1, kSlack);
+    }
     // The product-issuing part of the iteration runs at raised wave priority:
     // when both waves of a SIMD are ready, the one feeding the matrix core
     // issues first, and the other's bookkeeping fills the gaps.
@@ -342,9 +357,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       // The probabilities of slot 1 and the S products of slot 2 do not
       // depend on each other: interleave about six vector instructions after
       // each product so that they issue while it runs.
-      s_out = tail_and_s(s_in, neg_ref, pb, st2);
+      s_out = tail_and_s(s_in, neg_ref, pb, st2, rsum);
     } else if (pv) {
-      softmax_tail(s_in, neg_ref, pb);
+      rsum = softmax_tail(s_in, neg_ref, pb);
       asm volatile("" : "=v"(s_out));  // unused: defined without an instruction
     } else if (do_s) {
       u32x4 kf[8];
@@ -353,6 +368,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     } else {
       asm volatile("" : "=v"(s_out));  // unused: defined without an instruction
     }
+    if constexpr (SPARSE) {
+      // Rare: a row outran the reference.  Move each selected row's reference
+      // to its maximum (o and l rescaled) and form the probabilities again.
+      if (pv && __ballot(!(rsum <= kSlackSum))) {
+        neg_ref = softmax_head(s_in, qkey[1], mine1, 0.f);
+        rsum = softmax_tail(s_in, neg_ref, pb);
+      }
+    }
+    l += rsum;
     if (pv) mma_pv(st1, pb);
     __builtin_amdgcn_s_setprio(0);
 
