@@ -15,27 +15,12 @@ namespace solattn {
 // 256 threads = 16 row groups x 16 column chunks of 8 bf16 (16 B): every load
 // instruction of a wave reads 4 whole 256-byte rows (coalesced), and each
 // thread keeps all its row loads in flight before summing.
-// For V the block sum is also written, transposed and permuted, as bf16 for
-// the Taylor MFMA of the forward kernel.
 // ---------------------------------------------------------------------------
 template <int B>
 __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   __shared__ float part[16][kHeadDim + 4];
   const int j = blockIdx.x, h = blockIdx.y, which = blockIdx.z;
   const int tid = threadIdx.x, chunk = tid & 15, rg = tid >> 4;
-  if (j >= a.nb) {  // zero padding of the forward pass's bf16 copies
-    if (tid < kHeadDim) {
-      if (which == 1 && a.vsumT) {
-        const int pj = (j & ~15) + perm16(j & 15);
-        a.vsumT[((int64_t)h * kHeadDim + tid) * a.nb_pad + pj] = 0;
-      }
-      if (which == 0 && a.khi) {
-        a.khi[((int64_t)h * a.nb_pad + j) * kHeadDim + tid] = 0;
-        a.klo[((int64_t)h * a.nb_pad + j) * kHeadDim + tid] = 0;
-      }
-    }
-    return;
-  }
   const uint16_t* src = (which ? a.v : a.k) + ((int64_t)h * a.N + (int64_t)j * B) * kHeadDim;
   const int n = min(B, a.N - j * B);
   constexpr int R = B / 16;
@@ -62,29 +47,75 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += part[r][tid];
-    float mean = s / (float)n;
     float* dst = which ? a.vbar : a.kbar;
-    dst[((int64_t)h * a.nb + j) * kHeadDim + tid] = mean;
-    if (which == 1 && a.vsumT) {
-      const int pj = (j & ~15) + perm16(j & 15);
-      a.vsumT[((int64_t)h * kHeadDim + tid) * a.nb_pad + pj] = f32_to_bf16_bits(s);
-    }
-    if (which == 0 && a.khi) {
-      __bf16 hi, lo;
-      split_bf16(mean, hi, lo);
-      a.khi[((int64_t)h * a.nb_pad + j) * kHeadDim + tid] = __builtin_bit_cast(u16, hi);
-      a.klo[((int64_t)h * a.nb_pad + j) * kHeadDim + tid] = __builtin_bit_cast(u16, lo);
-    }
+    dst[((int64_t)h * a.nb + j) * kHeadDim + tid] = s / (float)n;
   }
 }
 
+// ---------------------------------------------------------------------------
+// Routing forms of the pooled blocks for the fused forward kernel.  One
+// workgroup per (16 consecutive blocks, head), blocks up to nb_pad:
+//  - khi / klo: the bf16 hi + lo parts of the pooled keys, rows past the last
+//    block zero (whole 16-byte stores);
+//  - vsumT: the value block sums n_j * vbar_j in bf16, transposed to
+//    [dim][block] with the blocks of each group of 16 permuted for the Taylor
+//    MFMA operand; staged in LDS so that each dimension's 32 bytes go out as
+//    two 16-byte stores.
+// The pool kernel itself only writes the fp32 means, coalesced.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void forms_kernel(PoolArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 vs[kHeadDim][16];
+  const int h = blockIdx.y, tid = threadIdx.x;
+  const int j0 = blockIdx.x * 16, jj = tid >> 4, c = (tid & 15) * 8, j = j0 + jj;
+  f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
+  float n = 0.f;
+  if (j < a.nb) {
+    const float* kb = a.kbar + ((int64_t)h * a.nb + j) * kHeadDim + c;
+    const float* vb = a.vbar + ((int64_t)h * a.nb + j) * kHeadDim + c;
+    k0 = *reinterpret_cast<const f32x4*>(kb);
+    k1 = *reinterpret_cast<const f32x4*>(kb + 4);
+    v0 = *reinterpret_cast<const f32x4*>(vb);
+    v1 = *reinterpret_cast<const f32x4*>(vb + 4);
+    n = (float)min(a.B, a.N - j * a.B);  // valid keys of the block
+  }
+  bf16x8 hi, lo;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    __bf16 hh, ll;
+    split_bf16(k0[e], hh, ll);
+    hi[e] = hh;
+    lo[e] = ll;
+    split_bf16(k1[e], hh, ll);
+    hi[e + 4] = hh;
+    lo[e + 4] = ll;
+  }
+  const int64_t ko = ((int64_t)h * a.nb_pad + j) * kHeadDim + c;
+  *reinterpret_cast<bf16x8*>(a.khi + ko) = hi;
+  *reinterpret_cast<bf16x8*>(a.klo + ko) = lo;
+  const int pj = perm16(jj);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    vs[c + e][pj] = f32_to_bf16_bits(v0[e] * n);
+    vs[c + 4 + e][pj] = f32_to_bf16_bits(v1[e] * n);
+  }
+  __syncthreads();
+  const int dim = tid >> 1, half = tid & 1;
+  *reinterpret_cast<u32x4*>(a.vsumT + ((int64_t)h * kHeadDim + dim) * a.nb_pad + j0 + half * 8) =
+      *reinterpret_cast<const u32x4*>(&vs[dim][half * 8]);
+}
+
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s) {
-  dim3 grid((a.vsumT || a.khi) ? a.nb_pad : a.nb, a.H, 2);
+  dim3 grid(a.nb, a.H, 2);
   if (a.B == 64)
     pool_kernel<64><<<grid, 256, 0, s>>>(a);
   else
     pool_kernel<128><<<grid, 256, 0, s>>>(a);
-  return hipGetLastError();
+  if (hipError_t e = hipGetLastError()) return e;
+  if (a.khi) {  // the forward pass's forms (khi, klo and vsumT are set together)
+    forms_kernel<<<dim3(a.nb_pad / 16, a.H), 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------
