@@ -39,8 +39,9 @@ constexpr int kUE = kU * kHeadDim;      // bf16 per tensor per stage
 constexpr int kRing = 5;                // LDS stages (80 KiB: two workgroups per CU)
 constexpr int kAhead = kRing - 1;       // units in flight beyond the one whose PV runs
 constexpr int kDmaPerUnit = 4;          // loads per wave per unit: 2 groups of 4 rows, K and V
-constexpr float kSlack = 8.f;           // log2 units the reference may lag the row max
-constexpr float kSlackSum = 256.f;      // 2^kSlack: bound on a lane's row sum of one unit
+// The running sums' reference may lag a row's maximum by up to 8 (log2
+// units): a lane's row sum of one unit's probabilities stays within 2^8.
+constexpr float kSlackSum = 256.f;
 constexpr int kLgkm0 = 0xC07F;          // s_waitcnt lgkmcnt(0)
 
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(n) alone.
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
   float l = 0.f;  // this lane's share of the denominator, relative to 2^m
-  float m;        // reference of the running sums (log2 units), within kSlack of the max
+  float m;        // reference of the running sums (log2 units), within 8 of the max
   float mu = 0.f, tau = __builtin_inff();
   if constexpr (SPARSE) {
     if (qvalid) {
@@ -197,13 +198,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     return s;
   };
 
-  // ---- online softmax of one unit's S tile, in two parts.  The head masks
-  // keys past the end, finds the row max and moves the reference (m, with o
-  // and l rescaled) when the max outruns it; it returns the exponent offset
-  // (-m, or -inf for rows that did not select the unit: p = 0).  The tail
-  // forms the probabilities as the bf16 B operand of the PV product (keys
-  // permuted within 16 as the accumulator layout holds them) and adds their
-  // row sums to l.
+  // ---- online softmax of one unit's S tile.  Keys past the end are masked
+  // first.  The tail forms the probabilities as the bf16 B operand of the PV
+  // product (keys permuted within 16 as the accumulator layout holds them)
+  // and returns their row sum.  The head, taken only when the probabilities
+  // against the current reference overran it, finds the row max and moves
+  // the reference (m, with o and l rescaled); it returns the exponent offset
+  // (-m, or -inf for rows that did not select the unit: p = 0).
   auto mask_ragged = [&](f32x16& s, int key0) __attribute__((always_inline)) {
     if (key0 + kU > Nk) {  // ragged last unit: keys past the end do not exist
       // element i holds key offset acc_row(i, 0) + 4g: compare the one
@@ -214,15 +215,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         if (g4 >= lim - acc_row(i, 0)) s[i] = -__builtin_inff();
     }
   };
-  auto softmax_head = [&](f32x16& s, int key0, bool mine, float slack) __attribute__((always_inline)) {
+  auto softmax_head = [&](f32x16& s, int key0, bool mine) __attribute__((always_inline)) {
     mask_ragged(s, key0);
     float mx = s[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
     mx = fmaxf(mx, partner_f(mx, g));
     const float mc = mx * sl2;
-    // move the reference only when the max outruns it by more than the slack
-    const bool up = mine && (mc > m + slack);
+    // each selected row's reference moves up to its maximum
+    const bool up = mine && (mc > m);
     if (__ballot(up)) {
       const float alpha = up ? fast_exp2(m - mc) : 1.f;
       l *= alpha;
@@ -338,16 +339,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     bf16x8 pb[2];
     float neg_ref = 0.f, rsum = 0.f;
     const bool mine1 = (qmine & 2u) != 0;
-    if constexpr (SPARSE) {
-      // The reference starts at mu (finite) and is checked after the fact: the
-      // probabilities are formed against it and the unit goes on only if every
-      // lane's row sum stays within 2^kSlack (which bounds each probability).
-      if (pv) {
-        mask_ragged(s_in, qkey[1]);
-        neg_ref = mine1 ? -m : -__builtin_inff();
-      }
-    } else {
-      if (pv) neg_ref = softmax_head(s_in, qkey[1], mine1, kSlack);
+    // The reference is checked after the fact: the probabilities are formed
+    // against it and the unit goes on only if every lane's row sum stays
+    // within kSlackSum (which bounds each probability).  A dense row's first
+    // unit always fails the check (its reference is still -inf) and sets it.
+    if (pv) {
+      mask_ragged(s_in, qkey[1]);
+      neg_ref = mine1 ? -m : -__builtin_inff();
     }
     // The product-issuing part of the iteration runs at raised wave priority:
     // when both waves of a SIMD are ready, the one feeding the matrix core
@@ -368,13 +366,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     } else {
       asm volatile("" : "=v"(s_out));  // unused: defined without an instruction
     }
-    if constexpr (SPARSE) {
-      // Rare: a row outran the reference.  Move each selected row's reference
-      // to its maximum (o and l rescaled) and form the probabilities again.
-      if (pv && __ballot(!(rsum <= kSlackSum))) {
-        neg_ref = softmax_head(s_in, qkey[1], mine1, 0.f);
-        rsum = softmax_tail(s_in, neg_ref, pb);
-      }
+    // Rare after a row's first unit: a row outran the reference.  Move each
+    // selected row's reference to its maximum (o and l rescaled) and form the
+    // probabilities again.
+    if (pv && __ballot(!(rsum <= kSlackSum))) {
+      neg_ref = softmax_head(s_in, qkey[1], mine1);
+      rsum = softmax_tail(s_in, neg_ref, pb);
     }
     l += rsum;
     if (pv) mma_pv(st1, pb);

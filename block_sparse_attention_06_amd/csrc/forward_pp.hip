@@ -25,7 +25,7 @@ namespace {
 constexpr int kPPUnit = 64;                          // keys per staged unit
 constexpr int kPPStages = 4;                         // LDS ring
 constexpr int kPPStageElems = kPPUnit * kHeadDim;    // bf16 per tensor per stage
-constexpr float kPPRescaleSlack = 8.f;               // log2 units the reference may lag the max
+constexpr float kPPSlackSum = 256.f;                 // 2^8: bound on a lane's row sum of one unit
 constexpr int kPPWaitNext = 0x0F74;                  // s_waitcnt vmcnt(4): next unit landed
 constexpr int kPPWaitLgkm0 = 0xC07F;                 // s_waitcnt lgkmcnt(0)
 
@@ -189,30 +189,13 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
   };
 
   // ---- phase B: online softmax of the scores in s (unit slot `su`) ----
-  auto phase_b = [&](int key0, bool mine, bool need) __attribute__((always_inline)) {
-    if (!need) return;
-    if (key0 + kPPUnit > Nk) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (key0 + kt * 32 + acc_row(i, g) >= Nk) s[kt][i] = -__builtin_inff();
-    }
-    float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
-    mx = fmaxf(mx, pp_partner(mx, g));
-    const float mc = mx * sl2;
-    const bool up = mine && (mc > m + kPPRescaleSlack);
-    if (__ballot(up)) {
-      // the accumulator is rescaled by phase A, before it adds this unit
-      const float alpha = up ? fast_exp2(m - mc) : 1.f;
-      l *= alpha;
-      o_scale *= alpha;
-      o_rescale = true;
-    }
-    if (up) m = mc;
-    const float neg_ref = mine ? -m : -__builtin_inff();
+  // The probabilities are formed against the current reference first; the
+  // unit goes on only if every lane's row sum stays within 2^slack (which
+  // bounds each probability).  Otherwise -- always on a row's first unit,
+  // whose reference is still -inf, and rarely after -- each selected row's
+  // reference moves to its maximum (the accumulator is rescaled by phase A,
+  // before it adds this unit) and the probabilities are formed again.
+  auto probs = [&](float neg_ref) __attribute__((always_inline)) -> float {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -228,7 +211,33 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
         const bf16x2 pr = {pb[t][2 * e], pb[t][2 * e + 1]};
         rsum[e] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rsum[e], false);
       }
-    l += (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
+    return (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
+  };
+  auto phase_b = [&](int key0, bool mine, bool need) __attribute__((always_inline)) {
+    if (!need) return;
+    if (key0 + kPPUnit > Nk) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (key0 + kt * 32 + acc_row(i, g) >= Nk) s[kt][i] = -__builtin_inff();
+    }
+    float rs = probs(mine ? -m : -__builtin_inff());
+    if (__ballot(!(rs <= kPPSlackSum))) {
+      float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
+      mx = fmaxf(mx, pp_partner(mx, g));
+      const float mc = mx * sl2;
+      const bool up = mine && (mc > m);
+      const float alpha = up ? fast_exp2(m - mc) : 1.f;  // 0 on a row's first unit
+      l *= alpha;
+      o_scale *= alpha;
+      o_rescale = true;
+      if (up) m = mc;
+      rs = probs(mine ? -m : -__builtin_inff());
+    }
+    l += rs;
   };
 
   // ---- prologue: units 0 and 1 into stages 0 and 1 ----
