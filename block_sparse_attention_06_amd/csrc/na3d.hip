@@ -42,7 +42,7 @@ __device__ __forceinline__ int n_vslot(int row, int c) { return c ^ ((row & 3) <
 
 __device__ __forceinline__ int win_start(int p, int len, int k) { return min(max(p - (k >> 1), 0), len - k); }
 
-constexpr float kSlack = 8.f;  // log2 units the reference may lag the row maximum
+constexpr float kSlackSum = 256.f;  // 2^8: the reference may lag the row maximum by 8 (log2 units)
 
 // Direct global -> LDS load of 16 bytes per lane from sbase + voff (sbase
 // wave-uniform, voff a 32-bit per-lane byte offset); lane l's bytes land at
@@ -149,8 +149,7 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
   // Running sums relative to a reference m (log2 units) that may lag the row
-  // maximum by up to kSlack: o and l are rescaled only when the maximum
-  // outruns it.  Two denominators: of the bf16 probabilities the PV product
+  // maximum by up to 8: o and l are rescaled only when the maximum outruns it.  Two denominators: of the bf16 probabilities the PV product
   // uses (the output's normaliser, so the weights sum to one exactly as
   // multiplied) and of the fp32 exponentials (for lse: with windows of a few
   // dozen keys the bf16 rounding of p would not average out).  m starts at a
@@ -204,49 +203,60 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
       s = mfma32(as_bf16x8(kf), qf.k[ks], s);
     }
     // rows of the unit inside this query's window (and not before the group's
-    // nominal start)
+    // nominal start); columns outside it carry the -inf column bias
     const int rlo = max(wy, ynom), rhi = wy + a.ky;
-    float mxr[UR];
+    float rbias[UR];
 #pragma unroll
-    for (int rr = 0; rr < UR; ++rr) mxr[rr] = -__builtin_inff();
+    for (int rr = 0; rr < UR; ++rr) rbias[rr] = (yy + rr >= rlo && yy + rr < rhi) ? 0.f : -__builtin_inff();
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s[i] += cbias[i % NC];
-      mxr[acc_row(i, 0) / UC] = fmaxf(mxr[acc_row(i, 0) / UC], s[i]);
-    }
-    float rbias[UR], mx = -__builtin_inff();
+    for (int i = 0; i < 16; ++i) s[i] += cbias[i % NC];
+    // Probabilities against the current reference first; the unit goes on
+    // only if the lane's bf16 row sum stays within kSlackSum (which bounds each
+    // probability).  Otherwise -- a query's first unit with keys in its window
+    // (the reference is still -1e30: the sums overflow), or rarely a query that
+    // outran it -- the row maxima move the reference and the probabilities
+    // are formed again.
+    bf16x8 pb[2];
+    float rs = 0.f, rs32 = 0.f;
+    auto probs = [&]() __attribute__((always_inline)) {
+      float nref[UR];
 #pragma unroll
-    for (int rr = 0; rr < UR; ++rr) {
-      rbias[rr] = (yy + rr >= rlo && yy + rr < rhi) ? 0.f : -__builtin_inff();
-      mx = fmaxf(mx, mxr[rr] + rbias[rr]);
-    }
-    // partner lane l ^ 32 holds the other 16 keys of the same query
-    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    const float mc = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * sl2;
-    const bool up = mc > m + kSlack;
-    if (__ballot(up)) {
+      for (int rr = 0; rr < UR; ++rr) nref[rr] = rbias[rr] - m;
+      rs = 0.f;
+      rs32 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float e0 = fast_exp2(__builtin_fmaf(s[i], sl2, nref[acc_row(i, 0) / UC]));
+        const float e1 = fast_exp2(__builtin_fmaf(s[i + 1], sl2, nref[acc_row(i + 1, 0) / UC]));
+        const __bf16 b0 = (__bf16)e0, b1 = (__bf16)e1;
+        pb[i >> 3][i & 7] = b0;
+        pb[i >> 3][(i & 7) + 1] = b1;
+        const bf16x2 pr2 = {b0, b1};
+        rs = __builtin_amdgcn_fdot2_f32_bf16(pr2, one2, rs, false);
+        rs32 += e0 + e1;
+      }
+    };
+    probs();
+    if (__ballot(!(rs <= kSlackSum))) {
+      float mxr[UR];
+#pragma unroll
+      for (int rr = 0; rr < UR; ++rr) mxr[rr] = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mxr[acc_row(i, 0) / UC] = fmaxf(mxr[acc_row(i, 0) / UC], s[i]);
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int rr = 0; rr < UR; ++rr) mx = fmaxf(mx, mxr[rr] + rbias[rr]);
+      // partner lane l ^ 32 holds the other 16 keys of the same query
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      const float mc = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * sl2;
+      const bool up = mc > m;
       const float alpha = up ? fast_exp2(m - mc) : 1.f;
       l *= alpha;
       l32 *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-    }
-    if (up) m = mc;
-    float nref[UR];
-#pragma unroll
-    for (int rr = 0; rr < UR; ++rr) nref[rr] = rbias[rr] - m;
-    bf16x8 pb[2];
-    float rs = 0.f, rs32 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const float e0 = fast_exp2(__builtin_fmaf(s[i], sl2, nref[acc_row(i, 0) / UC]));
-      const float e1 = fast_exp2(__builtin_fmaf(s[i + 1], sl2, nref[acc_row(i + 1, 0) / UC]));
-      const __bf16 b0 = (__bf16)e0, b1 = (__bf16)e1;
-      pb[i >> 3][i & 7] = b0;
-      pb[i >> 3][(i & 7) + 1] = b1;
-      const bf16x2 pr2 = {b0, b1};
-      rs = __builtin_amdgcn_fdot2_f32_bf16(pr2, one2, rs, false);
-      rs32 += e0 + e1;
+      if (up) m = mc;
+      probs();
     }
     l += rs;
     l32 += rs32;
