@@ -146,7 +146,7 @@ def test_dense_tiny_clustered():
 # ---------------------------------------------------------------------------
 
 
-def _sparse_case(Q, K, V, B, beta, heads=None, rows=None):
+def _sparse_case(Q, K, V, B, beta, heads=None, rows=None, lse_max=None):
     out, lse = sa.sol_attn_forward(dev(Q), dev(K), dev(V), B=B, beta=beta, mode=sa.SOL_SPARSE)
     torch.cuda.synchronize()
     go, gl = host(out), host(lse)
@@ -155,7 +155,8 @@ def _sparse_case(Q, K, V, B, beta, heads=None, rows=None):
         r = np.arange(Q.shape[1]) if rows is None else rows
         o, l, info, cands = sparse_with_ties(_head(Q, h), _head(K, h), _head(V, h), B, beta, r)
         ro, rl = best_match(go[h][r], gl[h][r], o, l, cands)
-        check_close(go[h][r], ro, gl[h][r], rl, what=f"sparse B{B} beta{beta} h{h}")
+        kw = {} if lse_max is None else {"lse_max": lse_max}
+        check_close(go[h][r], ro, gl[h][r], rl, what=f"sparse B{B} beta{beta} h{h}", **kw)
     return go, gl
 
 
@@ -195,6 +196,54 @@ def test_sparse_many_tiles(N, Nk, B, beta):
     H = 16
     Q, K, V = gaussian(H, N, 128, seed=N + Nk + B, nk=Nk)
     _sparse_case(Q, K, V, B, beta, heads=(0, H - 1))
+
+
+def _growing_logits(H, N, Nk, slope, seed):
+    """Logits that grow along the keys by about `slope` nats per key (q has a
+    component of 4 along dimension 0, key t one of 0.7 * slope / 0.25 * t):
+    at 0.25 nats per key every 32-key unit outruns the running reference by
+    more than 8 log2 units, so the softmax moves its reference on every unit."""
+    from synth import f32_to_bf16_bits
+    rng = np.random.default_rng(seed)
+    q = 0.3 * rng.standard_normal((H, N, 128)).astype(np.float32)
+    k = 0.3 * rng.standard_normal((H, Nk, 128)).astype(np.float32)
+    v = rng.standard_normal((H, Nk, 128)).astype(np.float32)
+    q[:, :, 0] = 4.0
+    k[:, :, 0] = (slope * math.sqrt(128) / 4.0) * np.arange(Nk, dtype=np.float32)
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
+def test_dense_reference_moves_on_every_unit():
+    """Dense mode with logits rising ~0.25 nats per key up to ~370: the
+    reference of the running sums is moved (and the sums rescaled) on every
+    unit, in the 4-wave kernel (short query set) and the ping-pong kernel.
+
+    lse is bounded by 2.5e-3 here instead of 1e-3: the kernels' denominator is
+    the sum of the bf16-rounded probabilities (the values the PV product
+    multiplies, so the output's weights sum to one), and with a handful of
+    keys carrying the mass their relative rounding (up to 2^-9 each) does not
+    average out in ln(l)."""
+    for H, N in ((2, 200), (16, 4096)):  # split keys / ping-pong kernel (256 workgroups)
+        Q, K, V = _growing_logits(H, N, 1500, 0.25, seed=N)
+        out, lse = sa.sol_attn_forward(dev(Q), dev(K), dev(V), mode=sa.SOL_DENSE)
+        torch.cuda.synchronize()
+        rows = np.arange(0, N, max(1, N // 200))
+        for h in (0, H - 1):
+            o, l = O.dense_head_ref(_head(Q, h), _head(K, h), _head(V, h), rows=rows)
+            check_close(host(out[h])[rows], o, host(lse[h])[rows], l, what=f"dense growing N{N} h{h}",
+                        lse_max=2.5e-3)
+
+
+@pytest.mark.parametrize("B", [64, 128])
+def test_sparse_reference_moves_on_every_unit(B):
+    """Sparse mode on the same rising logits: the reference starts at mu, far
+    below the selected blocks' scores, and moves on every selected unit; the
+    rejected early blocks' Taylor weights are negligible next to e^max.  lse
+    bound 2.5e-3 for the reason given in the dense case."""
+    Q, K, V = _growing_logits(2, 300, 1500, 0.25, seed=B)  # keys split over workgroups
+    _sparse_case(Q, K, V, B, 0.0, lse_max=2.5e-3)
+    Q, K, V = _growing_logits(16, 4096, 1500, 0.25, seed=B + 1)  # one workgroup per tile
+    _sparse_case(Q, K, V, B, 0.0, heads=(0, 15), rows=np.arange(0, 4096, 17), lse_max=2.5e-3)
 
 
 def test_sparse_split_keys_short_query():
