@@ -190,7 +190,7 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
 
   // ---- phase B: online softmax of the scores in s (unit slot `su`) ----
   // The probabilities are formed against the current reference first; the
-  // unit goes on only if every lane's row sum stays within 2^slack (which
+  // unit goes on only if every lane's row sum stays within kPPSlackSum (which
   // bounds each probability).  Otherwise -- always on a row's first unit,
   // whose reference is still -inf, and rarely after -- each selected row's
   // reference moves to its maximum (the accumulator is rescaled by phase A,

@@ -11,8 +11,11 @@ struct PoolArgs {
   const uint16_t* v;
   float* kbar;      // [H, nb, 128]
   float* vbar;      // [H, nb, 128]
-  uint16_t* vsumT;  // [H, 128, nb_pad] bf16 block sums, permuted groups of 16; may be null
-  uint16_t* khi;    // [H, nb_pad, 128] bf16 hi part of kbar (zero rows past nb); may be null
+  // The forward pass's routing forms, written by forms_kernel after the pool
+  // when khi is set (khi, klo and vsumT are set together; all null for the
+  // pool alone):
+  uint16_t* vsumT;  // [H, 128, nb_pad] bf16 block sums, permuted groups of 16
+  uint16_t* khi;    // [H, nb_pad, 128] bf16 hi part of kbar (zero rows past nb)
   uint16_t* klo;    // [H, nb_pad, 128] bf16 lo part
   int N, H, B, nb, nb_pad;
 };
