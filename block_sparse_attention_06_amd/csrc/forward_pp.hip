@@ -112,6 +112,11 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
   float o_scale = 1.f;     // pending rescale of o (set by phase B, applied by phase A)
   bool o_rescale = false;  // wave-uniform
   bf16x8 pb[4];
+  // V^T operands of the first two products of the next PV step, read at the
+  // end of the softmax phase of the same unit (its stage stays resident until
+  // that PV step has run)
+  constexpr int kVPre = 2;
+  u32x4 vpre[kVPre];
 #pragma unroll
   for (int i = 0; i < 4; ++i) pb[i] = bf16x8{};
 
@@ -166,9 +171,14 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
           const int roff = (kt * 32 + h2 * 16) * 256;
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) {
-            const u32x2 v0 = lds_read_tr16(reinterpret_cast<const u16*>(vst + vaddr(dt) + roff));
-            const u32x2 v1 = lds_read_tr16(reinterpret_cast<const u16*>(vst + vaddr(dt) + roff + 8 * 256));
-            const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
+            u32x4 va;
+            if (kt == 0 && h2 == 0 && dt < kVPre) {
+              va = vpre[dt];
+            } else {
+              const u32x2 v0 = lds_read_tr16(reinterpret_cast<const u16*>(vst + vaddr(dt) + roff));
+              const u32x2 v1 = lds_read_tr16(reinterpret_cast<const u16*>(vst + vaddr(dt) + roff + 8 * 256));
+              va = u32x4{v0[0], v0[1], v1[0], v1[1]};
+            }
             o[dt] = mfma32(as_bf16x8(va), pb[kt * 2 + h2], o[dt]);
           }
         }
@@ -213,7 +223,7 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
       }
     return (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
   };
-  auto phase_b = [&](int key0, bool mine, bool need) __attribute__((always_inline)) {
+  auto phase_b = [&](int key0, bool mine, bool need, int st) __attribute__((always_inline)) {
     if (!need) return;
     if (key0 + kPPUnit > Nk) {
 #pragma unroll
@@ -238,6 +248,13 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
       rs = probs(mine ? -m : -__builtin_inff());
     }
     l += rs;
+    const char* vst = lds_v_bytes + st * kStageBytes;
+#pragma unroll
+    for (int dt = 0; dt < kVPre; ++dt) {
+      const u32x2 v0 = lds_read_tr16(reinterpret_cast<const u16*>(vst + vaddr(dt)));
+      const u32x2 v1 = lds_read_tr16(reinterpret_cast<const u16*>(vst + vaddr(dt) + 8 * 256));
+      vpre[dt] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+    }
   };
 
   // ---- prologue: units 0 and 1 into stages 0 and 1 ----
@@ -280,9 +297,9 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
       if constexpr (GRP == 0) {
         phase_a(st_prev, st_cur);
         pp_barrier();
-        phase_b(qkey[1], qmine[1], qval[1] && qneed[1]);  // softmax of unit u
+        phase_b(qkey[1], qmine[1], qval[1] && qneed[1], st_cur);  // softmax of unit u
       } else {
-        phase_b(qkey[0], qmine[0], qval[0] && qneed[0]);  // softmax of unit u-1
+        phase_b(qkey[0], qmine[0], qval[0] && qneed[0], st_prev);  // softmax of unit u-1
         pp_barrier();
         phase_a(st_prev, st_cur);
       }
