@@ -15,9 +15,10 @@
 //
 // Workgroup: 4 waves x 32 query rows = 128 rows of one head; two workgroups
 // per CU.  Keys stream through LDS in units of 32 rows of K and V, in a ring of
-// five stages filled by direct global->LDS loads.  A load takes a scalar base
+// four stages filled by direct global->LDS loads.  A load takes a scalar base
 // (the unit's first key) and a per-lane offset fixed for the whole kernel, so
-// issuing a unit costs no vector arithmetic.
+// issuing a unit costs no vector arithmetic; the main loop is unrolled over
+// one turn of the ring, so stage offsets are immediates in every LDS access.
 //
 // Per iteration each wave (1) runs the online softmax of the oldest unit in
 // flight on its S tile, computed one iteration earlier, (2) routes and issues
@@ -36,7 +37,7 @@ namespace {
 
 constexpr int kU = 32;                  // keys per staged unit
 constexpr int kUE = kU * kHeadDim;      // bf16 per tensor per stage
-constexpr int kRing = 5;                // LDS stages (80 KiB: two workgroups per CU)
+constexpr int kRing = 4;                // LDS stages (64 KiB: two workgroups per CU)
 constexpr int kAhead = kRing - 1;       // units in flight beyond the one whose PV runs
 constexpr int kDmaPerUnit = 4;          // loads per wave per unit: 2 groups of 4 rows, K and V
 // The running sums' reference may lag a row's maximum by up to 8 (log2
@@ -186,10 +187,27 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   // ---- S^T = K Q^T of one staged unit (consumed an iteration later): operand
   // reads and products separately, so the products can be interleaved with
   // other work.
+  // Byte offsets, within a stage, of this lane's K operand of each k-step and
+  // of its V^T operand of each 32-dim tile (k-step h2 and the second 8 rows
+  // add constants): formed once, so that each operand read is one register
+  // plus an immediate (the stage offsets are compile-time in the unrolled loop).
+  uint32_t kofs[8], vofs[4];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) kofs[ks] = (uint32_t)(r32 * kHeadDim + (kslot(r32, ks * 2 + g) << 3)) * 2u;
+  {
+    const int G = lane >> 4, j = lane & 15, r0 = g * 4 + (j >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int col = dt * 32 + (G & 1) * 16 + 4 * (j & 3);
+      vofs[dt] = (uint32_t)(r0 * kHeadDim + (vslot(r0, col >> 3) << 3) + (col & 7)) * 2u;
+    }
+  }
+  auto kop = [&](int st, int ks) __attribute__((always_inline)) {
+    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(&lds_k[st][0]) + kofs[ks]);
+  };
   auto read_k = [&](int st, u32x4 (&kf)[8]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      kf[ks] = *reinterpret_cast<const u32x4*>(&lds_k[st][r32 * kHeadDim + (kslot(r32, ks * 2 + g) << 3)]);
+    for (int ks = 0; ks < 8; ++ks) kf[ks] = kop(st, ks);
   };
   auto mfma_s = [&](const u32x4 (&kf)[8]) __attribute__((always_inline)) {
     f32x16 s = {};
@@ -259,17 +277,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   auto tail_and_s = [&](const f32x16& s_in, float neg_ref, bf16x8 (&pb)[2], int st, float& rsum) __attribute__((always_inline)) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-    auto kaddr = [&](int ks) __attribute__((always_inline)) {
-      return reinterpret_cast<const u32x4*>(&lds_k[st][r32 * kHeadDim + (kslot(r32, ks * 2 + g) << 3)]);
-    };
     u32x4 kf[8];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kf[ks] = *kaddr(ks);
+    for (int ks = 0; ks < 4; ++ks) kf[ks] = kop(st, ks);
     f32x16 s = {};
     float rs[2] = {0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      if (k < 4) kf[k + 4] = *kaddr(k + 4);
+      if (k < 4) kf[k + 4] = kop(st, k + 4);
       s = mfma32(as_bf16x8(kf[k]), qf.k[k], s);
       __builtin_amdgcn_sched_barrier(0);
       const float e0 = fast_exp2(__builtin_fmaf(s_in[2 * k], sl2, neg_ref));
@@ -289,16 +304,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   // h2*16 + {4g..4g+3, 8+4g..8+4g+3} -- the keys of P this lane half holds --
   // read as two transposed 4 x 16 blocks per 16-lane group.
   auto mma_pv = [&](int st, const bf16x8 (&pb)[2]) __attribute__((always_inline)) {
-    const int G = lane >> 4, j = lane & 15;
+    const char* vst = reinterpret_cast<const char*>(&lds_v[st][0]);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const int r0 = h2 * 16 + g * 4 + (j >> 2);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const int col = dt * 32 + (G & 1) * 16 + 4 * (j & 3);
-        const u32x2 v0 = lds_read_tr16(&lds_v[st][r0 * kHeadDim + (vslot(r0, col >> 3) << 3) + (col & 7)]);
-        const u32x2 v1 =
-            lds_read_tr16(&lds_v[st][(r0 + 8) * kHeadDim + (vslot(r0 + 8, col >> 3) << 3) + (col & 7)]);
+        const char* a = vst + vofs[dt] + h2 * 16 * kHeadDim * 2;
+        const u32x2 v0 = lds_read_tr16(reinterpret_cast<const u16*>(a));
+        const u32x2 v1 = lds_read_tr16(reinterpret_cast<const u16*>(a + 8 * kHeadDim * 2));
         const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
         o[dt] = mfma32(as_bf16x8(va), pb[h2], o[dt]);
       }
@@ -315,7 +328,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i <= kAhead; ++i) qkey[i] = 0;
   uint32_t qneed = 0, qval = 0, qmine = 0;
-  int st_issue = 0;
   bool stream_done = false;
 
   // unit sources
@@ -332,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   // One iteration.  s_in holds the S tile of slot 1, s_out receives that of
   // slot 2; the loop below alternates the two tiles so that neither is copied.
   // Returns false once the stream is exhausted and every unit is through its PV.
-  auto iteration = [&](f32x16& s_in, f32x16& s_out) __attribute__((always_inline)) -> bool {
+  auto iteration = [&](f32x16& s_in, f32x16& s_out, const int st_issue) __attribute__((always_inline)) -> bool {
     const int st1 = st_issue == kRing - 1 ? 0 : st_issue + 1;
     const int st2 = st1 == kRing - 1 ? 0 : st1 + 1;
     const bool pv = (qneed & 2u) != 0, do_s = (qneed & 4u) != 0;
@@ -492,14 +504,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     qval = (qval >> 1) | ((uint32_t)have << kAhead);
     qneed = (qneed >> 1) | ((uint32_t)(have && ne) << kAhead);
     qmine = (qmine >> 1) | ((uint32_t)(have && mi) << kAhead);
-    st_issue = st1;  // slot 1's stage (slot 0 after the shift) is refilled next
     __builtin_amdgcn_s_waitcnt(kWaitNext);  // this wave's loads of the next two units landed
     wg_barrier();                           // ... and every wave's
     // done when the stream is exhausted and no issued unit awaits its PV
     return !(stream_done && (qval >> 1) == 0);
   };
   f32x16 sA = {}, sB = {};
-  while (iteration(sA, sB) && iteration(sB, sA)) {
+  // Iteration i refills stage i mod kRing (slot 1's stage becomes slot 0
+  // after the shift); the loop is unrolled over one turn of the ring so that
+  // every stage index, and with it every LDS address offset and every load's
+  // LDS destination, is a compile-time constant.
+  static_assert(kRing == 4, "the loop below is one turn of a four-stage ring");
+  while (iteration(sA, sB, 0) && iteration(sB, sA, 1) && iteration(sA, sB, 2) && iteration(sB, sA, 3)) {
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
 
