@@ -16,7 +16,8 @@
 // the four frames.  Keys stream through LDS as units of 32 keys -- UR rows of
 // UC consecutive columns of one frame (2 x 16 when the patch's columns fit in
 // 16, else 1 x 32) -- in a ring of kNRing stages filled by direct global->LDS
-// loads kNRing - 1 units ahead.  A wave skips the products of units outside
+// loads kNRing - 1 units ahead (the unit loop is unrolled over one turn of the
+// ring, so stage offsets are immediates).  A wave skips the products of units outside
 // its frame window; inside a unit, keys outside a query's window get
 // probability 0.
 #include "device.hpp"
@@ -182,8 +183,24 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
     dma_unit(min(lf, fb - 1), lf < fb ? ly : yb - 1, i);
     advance(lf, ly);
   }
-  for (int u = 0; u < nunits; ++u) {
-    const int st = u % kNRing;
+  // Byte offsets, within a stage, of this lane's K operand of each k-step and
+  // of its V^T operand of each 32-dim tile (k-step h2 and the second 8 rows
+  // add constants), formed once.
+  uint32_t nkofs[8], nvofs[4];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) nkofs[ks] = (uint32_t)(r32 * kHeadDim + (n_kslot(r32, ks * 2 + g) << 3)) * 2u;
+  {
+    const int G = lane >> 4, j = lane & 15, r0 = g * 4 + (j >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int col = dt * 32 + (G & 1) * 16 + 4 * (j & 3);
+      nvofs[dt] = (uint32_t)(r0 * kHeadDim + (n_vslot(r0, col >> 3) << 3) + (col & 7)) * 2u;
+    }
+  }
+  // One unit; st = u mod kNRing.  The loop below is unrolled over one turn of
+  // the ring, so st is a compile-time constant in each copy and every LDS
+  // access and load destination takes an immediate stage offset.
+  auto unit_step = [&](const int u, const int st) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(kNWait);  // this wave's loads of unit u landed
     __builtin_amdgcn_s_barrier();        // ... and every wave's; unit u - 1's stage is free
     asm volatile("" ::: "memory");
@@ -192,14 +209,14 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
     advance(lf, ly);
     const int ff = cf, ynom = cy;
     advance(cf, cy);
-    if (!wvalid || ff < wf || ff >= wf + a.kt) continue;  // wave-uniform
+    if (!wvalid || ff < wf || ff >= wf + a.kt) return;  // wave-uniform
     const int yy = min(ynom, ylast);
 
     // S^T = K Q^T for the unit's 32 keys
     f32x16 s = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const u32x4 kf = *reinterpret_cast<const u32x4*>(&lds_k[st][r32 * kHeadDim + (n_kslot(r32, ks * 2 + g) << 3)]);
+      const u32x4 kf = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(&lds_k[st][0]) + nkofs[ks]);
       s = mfma32(as_bf16x8(kf), qf.k[ks], s);
     }
     // rows of the unit inside this query's window (and not before the group's
@@ -262,18 +279,23 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
     l32 += rs32;
     // O^T += V^T P^T (as in the attention kernels: two transposing reads per
     // 16-key half and 32-dim tile)
-    const int G = lane >> 4, j = lane & 15;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const int r0 = h2 * 16 + g * 4 + (j >> 2);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const int col = dt * 32 + (G & 1) * 16 + 4 * (j & 3);
-        const u32x2 v0 = lds_read_tr16(&lds_v[st][r0 * kHeadDim + (n_vslot(r0, col >> 3) << 3) + (col & 7)]);
-        const u32x2 v1 = lds_read_tr16(&lds_v[st][(r0 + 8) * kHeadDim + (n_vslot(r0 + 8, col >> 3) << 3) + (col & 7)]);
+        const char* va = reinterpret_cast<const char*>(&lds_v[st][0]) + nvofs[dt] + h2 * 16 * kHeadDim * 2;
+        const u32x2 v0 = lds_read_tr16(reinterpret_cast<const u16*>(va));
+        const u32x2 v1 = lds_read_tr16(reinterpret_cast<const u16*>(va + 8 * kHeadDim * 2));
         o[dt] = mfma32(as_bf16x8(u32x4{v0[0], v0[1], v1[0], v1[1]}), pb[h2], o[dt]);
       }
     }
+    };
+  static_assert(kNRing == 4, "the loop below is one turn of a four-stage ring");
+  for (int u = 0; u < nunits; u += kNRing) {
+    unit_step(u, 0);
+    if (u + 1 < nunits) unit_step(u + 1, 1);
+    if (u + 2 < nunits) unit_step(u + 2, 2);
+    if (u + 3 < nunits) unit_step(u + 3, 3);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
 
