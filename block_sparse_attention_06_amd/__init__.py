@@ -130,11 +130,31 @@ def _want(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
         raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
 
 
+def _want_shape(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> None:
+    """As _want, and the exact shape: the kernels index every buffer by the
+    sizes passed alongside it, so a smaller tensor would be read or written
+    out of bounds."""
+    _want(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _want_ws(workspace: Optional[torch.Tensor]) -> int:
+    """Bytes of a caller's workspace (device memory, contiguous), 0 if None."""
+    if workspace is None:
+        return 0
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+        raise ValueError("workspace must be a GPU tensor")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace.numel() * workspace.element_size()
+
+
 def sol_attn_pool(k: torch.Tensor, v: torch.Tensor, B: int, stream=None):
     """Block means ``(kbar, vbar)`` ``[H, ceil(N/B), 128]`` fp32 of keys and values."""
     lib = load_library()
     _want(k, "k", torch.bfloat16, 3)
-    _want(v, "v", torch.bfloat16, 3)
+    _want_shape(v, "v", torch.bfloat16, k.shape)
     H, N, d = k.shape
     nb = (N + B - 1) // B
     kbar = torch.empty((H, nb, d), dtype=torch.float32, device=k.device)
@@ -148,8 +168,8 @@ def sol_attn_row_stats(q: torch.Tensor, kbar: torch.Tensor, B: int, Nk: int, str
     """``(mu, sigma)`` ``[H, N]`` fp32 of the block proxy scores of every query row."""
     lib = load_library()
     _want(q, "q", torch.bfloat16, 3)
-    _want(kbar, "kbar", torch.float32, 3)
     H, N, d = q.shape
+    _want_shape(kbar, "kbar", torch.float32, (H, (int(Nk) + B - 1) // B, d))
     mu = torch.empty((H, N), dtype=torch.float32, device=q.device)
     sigma = torch.empty_like(mu)
     _check("sol_attn_row_stats", lib.sol_attn_row_stats(
@@ -165,16 +185,17 @@ def sol_attn_row_stats_moment(q: torch.Tensor, kbar: torch.Tensor, B: int, Nk: i
     when not given."""
     lib = load_library()
     _want(q, "q", torch.bfloat16, 3)
-    _want(kbar, "kbar", torch.float32, 3)
     H, N, d = q.shape
+    _want_shape(kbar, "kbar", torch.float32, (H, (int(Nk) + B - 1) // B, d))
     need = H * (2 * d * d * 2 + d * 4 + 8 * (d * d + 2 * d) * 4)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    have = _want_ws(workspace)
     mu = torch.empty((H, N), dtype=torch.float32, device=q.device)
     sigma = torch.empty_like(mu)
     _check("sol_attn_row_stats_moment", lib.sol_attn_row_stats_moment(
         _ptr(q), _ptr(kbar), _ptr(mu), _ptr(sigma), N, int(Nk), H, d, int(B),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ptr(workspace), have, _stream(stream)))
     return mu, sigma
 
 
@@ -207,10 +228,12 @@ def sol_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, B: int =
             raise ValueError("out must have q's shape")
     if lse is None and want_lse:
         lse = torch.empty((H, N), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _want_shape(lse, "lse", torch.float32, (H, N))
     ws_bytes = sol_attn_workspace_size(N, Nk, H, d, B, mode)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    have = _want_ws(workspace)
     if math.isnan(beta):
         raise ValueError("beta must not be NaN")
     _check("sol_attn_forward", lib.sol_attn_forward(
@@ -224,15 +247,17 @@ def attn_lse_merge(out_a: torch.Tensor, lse_a: torch.Tensor, out_b: torch.Tensor
                    lse: Optional[torch.Tensor] = None, stream=None):
     """Exact merge of two partial answers over disjoint keys; returns ``(out, lse)``."""
     lib = load_library()
-    for t, n in ((out_a, "out_a"), (out_b, "out_b")):
-        _want(t, n, torch.bfloat16, 3)
-    for t, n in ((lse_a, "lse_a"), (lse_b, "lse_b")):
-        _want(t, n, torch.float32, 2)
+    _want(out_a, "out_a", torch.bfloat16, 3)
     H, N, d = out_a.shape
+    _want_shape(out_b, "out_b", torch.bfloat16, (H, N, d))
+    _want_shape(lse_a, "lse_a", torch.float32, (H, N))
+    _want_shape(lse_b, "lse_b", torch.float32, (H, N))
     if out is None:
         out = torch.empty_like(out_a)
+    _want_shape(out, "out", torch.bfloat16, (H, N, d))
     if lse is None:
         lse = torch.empty_like(lse_a)
+    _want_shape(lse, "lse", torch.float32, (H, N))
     _check("attn_lse_merge", lib.attn_lse_merge(
         _ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), _ptr(out), _ptr(lse), N, H, d,
         _stream(stream)))
@@ -269,16 +294,17 @@ def sol_attn_forward_shard(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if kbar_all is not None:
         _want(kbar_all, "kbar_all", torch.float32, 3)
         nb_all = kbar_all.shape[1]
+        _want_shape(kbar_all, "kbar_all", torch.float32, (H, nb_all, d))
     if part_o is None:
         part_o = torch.empty((H, N, d), dtype=torch.float32, device=q.device)
     if part_ml is None:
         part_ml = torch.empty((H, N, 2), dtype=torch.float32, device=q.device)
-    _want(part_o, "part_o", torch.float32, 3)
-    _want(part_ml, "part_ml", torch.float32, 3)
+    _want_shape(part_o, "part_o", torch.float32, (H, N, d))
+    _want_shape(part_ml, "part_ml", torch.float32, (H, N, 2))
     ws_bytes = sol_attn_shard_workspace_size(N, Nk, nb_all, H, d, B, beta)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    have = _want_ws(workspace)
     _check("sol_attn_forward_shard", lib.sol_attn_forward_shard(
         _ptr(q), _ptr(k), _ptr(v), _ptr(kbar_all), _ptr(part_o), _ptr(part_ml), N, Nk, nb_all,
         H, d, int(B), float(beta), _ptr(workspace), have, _stream(stream)))
@@ -298,6 +324,7 @@ def sol_attn_combine_partials(part_o: torch.Tensor, part_ml: torch.Tensor,
         raise ValueError("part_ml must be [S, H, N, 2]")
     if out is None:
         out = torch.empty((H, N, d), dtype=torch.bfloat16, device=part_o.device)
+    _want_shape(out, "out", torch.bfloat16, (H, N, d))
     lse = torch.empty((H, N), dtype=torch.float32, device=part_o.device) if want_lse else None
     _check("sol_attn_combine_partials", lib.sol_attn_combine_partials(
         _ptr(part_o), _ptr(part_ml), S, _ptr(out), _ptr(lse), N, H, d, _stream(stream)))
@@ -309,10 +336,12 @@ def sol_attn_proxy_scores(q: torch.Tensor, kbar: torch.Tensor, B: int, Nk: int,
     """Proxy scores ``[H, nrows, nb]`` fp32 as the forward kernel computes them."""
     lib = load_library()
     _want(q, "q", torch.bfloat16, 3)
-    _want(kbar, "kbar", torch.float32, 3)
     H, N, d = q.shape
     nrows = N - row0 if nrows is None else nrows
+    if row0 < 0 or nrows < 0 or row0 + nrows > N:
+        raise ValueError("rows [row0, row0 + nrows) must lie within [0, N)")
     nb = (Nk + B - 1) // B
+    _want_shape(kbar, "kbar", torch.float32, (H, nb, d))
     p = torch.empty((H, nrows, nb), dtype=torch.float32, device=q.device)
     _check("sol_attn_proxy_scores", lib.sol_attn_proxy_scores(
         _ptr(q), _ptr(kbar), _ptr(p), int(row0), int(nrows), N, int(Nk), H, d, int(B),
@@ -327,10 +356,14 @@ def sol_attn_block_mask(q: torch.Tensor, kbar: torch.Tensor, mu: torch.Tensor,
     (selected pairs, 32-row tile pairs, 128-row tile pairs, 128-row tile total)."""
     lib = load_library()
     _want(q, "q", torch.bfloat16, 3)
-    _want(kbar, "kbar", torch.float32, 3)
     H, N, d = q.shape
     nrows = N - row0 if nrows is None else nrows
+    if row0 < 0 or nrows < 0 or row0 + nrows > N:
+        raise ValueError("rows [row0, row0 + nrows) must lie within [0, N)")
     nb = (Nk + B - 1) // B
+    _want_shape(kbar, "kbar", torch.float32, (H, nb, d))
+    _want_shape(mu, "mu", torch.float32, (H, N))
+    _want_shape(sigma, "sigma", torch.float32, (H, N))
     mask = torch.empty((H, nrows, nb), dtype=torch.uint8, device=q.device) if want_mask else None
     counts = torch.empty(4, dtype=torch.int64, device=q.device)
     _check("sol_attn_block_mask", lib.sol_attn_block_mask(
@@ -375,7 +408,7 @@ def fp8_gemm_rowscale(a: torch.Tensor, sa: torch.Tensor, w: torch.Tensor, sw: to
         raise ValueError("fp8_gemm_rowscale: shape mismatch")
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    _want(out, "out", torch.bfloat16, 2)
+    _want_shape(out, "out", torch.bfloat16, (M, N))
     _check("fp8_gemm_rowscale", lib.fp8_gemm_rowscale(_ptr(a), _ptr(sa), _ptr(w), _ptr(sw),
                                                       _ptr(out), M, N, K, _stream(stream)))
     return out
@@ -395,6 +428,7 @@ def na3d_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, grid, window
         raise ValueError("na3d_forward: shapes do not match the grid")
     if out is None:
         out = torch.empty_like(q)
+    _want_shape(out, "out", torch.bfloat16, (H, n, d))
     lse = torch.empty((H, n), dtype=torch.float32, device=q.device) if want_lse else None
     _check("na3d_forward", lib.na3d_forward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse) if lse is not None else None,

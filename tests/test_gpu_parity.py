@@ -337,3 +337,32 @@ def test_error_codes_through_binding():
     with pytest.raises(sa.SolAttnError) as e:
         sa.sol_attn_forward(q, q, q, B=64, beta=0.0, workspace=small_ws)
     assert e.value.code == -1
+
+
+def test_binding_rejects_mis_sized_buffers():
+    """Buffers smaller than the sizes passed with them, or a workspace in host
+    memory, are refused by the binding before any launch (the C ABI takes
+    plain pointers and cannot check them)."""
+    H, N = 2, 256
+    q = torch.zeros((H, N, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        sa.sol_attn_forward(q, q, q, B=64, beta=0.0, lse=torch.empty((H, N - 1), device="cuda"))
+    with pytest.raises(ValueError):
+        sa.sol_attn_forward(q, q, q, B=64, beta=0.0,
+                            workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    lse = torch.zeros((H, N), device="cuda")
+    with pytest.raises(ValueError):
+        sa.attn_lse_merge(q, lse, q[:, :128].contiguous(), lse)
+    with pytest.raises(ValueError):
+        sa.attn_lse_merge(q, lse, q, lse, out=torch.empty_like(q)[:1].contiguous())
+    kbar, _ = sa.sol_attn_pool(q, q, 64)
+    with pytest.raises(ValueError):
+        sa.sol_attn_row_stats(q, kbar[:, :-1].contiguous(), 64, N)
+    with pytest.raises(ValueError):
+        sa.sol_attn_proxy_scores(q, kbar, 64, N, row0=200, nrows=100)
+    with pytest.raises(ValueError):
+        sa.sol_attn_pool(q, q[:, :100].contiguous(), 64)
+    # correctly sized buffers still work
+    out, l2 = sa.sol_attn_forward(q, q, q, B=64, beta=0.0, lse=torch.empty((H, N), device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.isfinite(l2).all()
