@@ -34,6 +34,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import bf16_to_f64
+
 __all__ = [
     "E4M3_MAX",
     "e4m3_decode",
@@ -84,7 +86,7 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
 def quantize_rows_ref(x_bits: np.ndarray):
     """Per-row FP8 quantisation of a bf16 matrix ``[M, K]`` (given as uint16
     bit patterns).  Returns ``(codes [M, K] uint8, scale [M] float32)``."""
-    x = (np.asarray(x_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    x = bf16_to_f64(x_bits).astype(np.float32)  # exact: every bf16 value is an fp32 value
     amax = np.abs(x).max(axis=1).astype(np.float32)
     safe = np.where(amax > 0, amax, np.float32(1))
     inv = np.where(amax > 0, np.float32(E4M3_MAX) / safe, np.float32(0)).astype(np.float32)

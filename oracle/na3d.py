@@ -26,6 +26,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import bf16_to_f64
+
 __all__ = ["window_start", "na3d_head_ref", "na3d_ref"]
 
 
@@ -70,8 +72,7 @@ def na3d_head_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, grid, window, row
 def na3d_ref(Q, K, V, grid, window, heads=None, rows=None):
     """All heads of bf16 bit arrays ``[H, T*Y*X, d]`` (uint16); returns fp64
     ``(out, lse)`` stacked over the heads requested."""
-    def f64(b):
-        return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     heads = range(Q.shape[0]) if heads is None else heads
-    res = [na3d_head_ref(f64(Q[h]), f64(K[h]), f64(V[h]), grid, window, rows) for h in heads]
+    res = [na3d_head_ref(bf16_to_f64(Q[h]), bf16_to_f64(K[h]), bf16_to_f64(V[h]), grid, window, rows)
+           for h in heads]
     return np.stack([r[0] for r in res]), np.stack([r[1] for r in res])

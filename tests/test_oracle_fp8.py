@@ -159,6 +159,7 @@ def _mutant_module(kind):
     src = open(path).read()
     assert src.count(old) == 1, kind
     m = types.ModuleType(f"fp8_mutant_{kind}")
+    m.__package__ = "oracle"  # the copy imports the oracle's pinned bf16 decoder
     exec(compile(src.replace(old, new), f"<fp8 mutant {kind}>", "exec"), m.__dict__)
     return m
 
@@ -179,6 +180,7 @@ def test_planted_mistakes_are_caught(kind):
 def test_unmutated_copy_passes_every_pin():
     """The copying mechanism itself changes nothing."""
     m = types.ModuleType("fp8_copy")
+    m.__package__ = "oracle"
     path = os.path.join(os.path.dirname(F0.__file__), "fp8.py")
     exec(compile(open(path).read(), "<fp8 copy>", "exec"), m.__dict__)
     for pin in PINS.values():
