@@ -164,6 +164,56 @@ __device__ __forceinline__ void dma_to_lds16(const void* gptr, uint32_t lds_base
                : "memory", "m0");
 }
 
+// Direct global -> LDS load of 16 bytes per lane from sbase + voff (sbase
+// wave-uniform, voff a 32-bit per-lane byte offset): one scalar base per
+// issue, no vector address arithmetic.  Lane l's bytes land at LDS byte
+// address lds + 16 l.  Ordered by the caller's explicit vmcnt waits and
+// barriers, as dma_to_lds16.
+__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// LDS layouts of a staged key/value unit ([keys][128 bf16], 16-byte chunks)
+// in the attention kernels: K rows put chunk c at c ^ (row % 16), so the S
+// operand reads 16 consecutive rows at one chunk without bank conflicts; V
+// rows put chunk c at c ^ 4 (row % 4), so the transposing read of 4
+// consecutive rows x 4 chunks per 16 lanes is conflict-free.
+__device__ __forceinline__ int kslot(int row, int c) { return c ^ (row & 15); }
+__device__ __forceinline__ int vslot(int row, int c) { return c ^ ((row & 3) << 2); }
+
+// Value held by the partner lane l ^ 32 (lane half g = l / 32): the two
+// halves of a query row's accumulators in the transposed MFMA layout.
+__device__ __forceinline__ float partner_f(float x, int g) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(g ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ uint32_t partner_b(uint32_t x, int g) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return g ? r[0] : r[1];
+}
+
+// Sum and maximum over the lane pair (l, l ^ 32); the same value in both lanes.
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Workgroup barrier that is also a compiler barrier for memory accesses (the
+// hardware barrier alone does not stop the compiler from moving LDS reads).
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // LDS byte address of a pointer into __shared__ memory.
 template <class T>
 __device__ __forceinline__ uint32_t lds_addr(const T* p) {

@@ -51,44 +51,6 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 // after) must have landed; the kAhead - 2 younger units may still be in flight.
 constexpr int kWaitNext = vmcnt_imm(kDmaPerUnit * (kAhead - 2));
 
-// LDS layouts of a unit ([32 rows][128 bf16], 16-byte chunks): K rows put
-// chunk c at c ^ (row % 16), so the S operand reads 16 consecutive rows at one
-// chunk without bank conflicts; V rows put chunk c at c ^ 4 (row % 4), so the
-// transposing read of 4 consecutive rows x 4 chunks per 16 lanes is
-// conflict-free.
-__device__ __forceinline__ int kslot(int row, int c) { return c ^ (row & 15); }
-__device__ __forceinline__ int vslot(int row, int c) { return c ^ ((row & 3) << 2); }
-
-// Direct global -> LDS load of 16 bytes per lane from sbase + voff (sbase
-// wave-uniform, voff a 32-bit per-lane byte offset); lane l's bytes land at LDS
-// byte address lds + 16 l.  Inline assembly keeps the compiler from treating
-// it as a pending write to all of LDS; the caller orders it with explicit
-// vector-memory waits and barriers.
-__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ float partner_f(float x, int g) {
-  // value of lane l ^ 32
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(g ? r[0] : r[1]);
-}
-
-__device__ __forceinline__ uint32_t partner_b(uint32_t x, int g) {
-  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return g ? r[0] : r[1];
-}
-
-// Workgroup barrier that is also a compiler barrier for memory accesses (the
-// hardware barrier alone does not stop the compiler from moving LDS reads).
-__device__ __forceinline__ void wg_barrier() {
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 }  // namespace
 
 template <bool SPARSE, int KB>
@@ -558,13 +520,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
 hipError_t launch_forward(const FwdArgs& a, bool sparse, int B, hipStream_t s) {
   const int grid = (a.total + 7) & ~7;
-  if (!sparse)
-    fwd_kernel<false, 128><<<grid, 256, 0, s>>>(a);
-  else if (B == 64)
-    fwd_kernel<true, 64><<<grid, 256, 0, s>>>(a);
-  else
-    fwd_kernel<true, 128><<<grid, 256, 0, s>>>(a);
-  return hipGetLastError();
+  if (!sparse) return launch_kernel(fwd_kernel<false, 128>, dim3(grid), dim3(256), s, a);
+  if (B == 64) return launch_kernel(fwd_kernel<true, 64>, dim3(grid), dim3(256), s, a);
+  return launch_kernel(fwd_kernel<true, 128>, dim3(grid), dim3(256), s, a);
 }
 
 }  // namespace solattn

@@ -29,19 +29,6 @@ constexpr float kPPSlackSum = 256.f;                 // 2^8: bound on a lane's r
 constexpr int kPPWaitNext = 0x0F74;                  // s_waitcnt vmcnt(4): next unit landed
 constexpr int kPPWaitLgkm0 = 0xC07F;                 // s_waitcnt lgkmcnt(0)
 
-__device__ __forceinline__ int pp_kslot(int row, int c) { return c ^ (row & 15); }
-__device__ __forceinline__ int pp_vslot(int row, int c) { return c ^ ((row & 3) << 2); }
-
-__device__ __forceinline__ float pp_partner(float x, int g) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(g ? r[0] : r[1]);
-}
-
-__device__ __forceinline__ uint32_t pp_partner_u(uint32_t x, int g) {
-  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return g ? r[0] : r[1];
-}
-
 // barrier that also pins the compiler's schedule on both sides
 __device__ __forceinline__ void pp_barrier() {
   __builtin_amdgcn_sched_barrier(0);
@@ -94,8 +81,8 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
       const int r0 = wave * 8 + i * 4;
       const int r = r0 + (lane >> 4), slot = lane & 15;
       const int64_t key = min(key0 + r, Nk - 1);
-      dma_to_lds16(kh + key * kHeadDim + (pp_kslot(r, slot) << 3), lds_addr(&lds_k[st][r0 * kHeadDim]));
-      dma_to_lds16(vh + key * kHeadDim + (pp_vslot(r, slot) << 3), lds_addr(&lds_v[st][r0 * kHeadDim]));
+      dma_to_lds16(kh + key * kHeadDim + (kslot(r, slot) << 3), lds_addr(&lds_k[st][r0 * kHeadDim]));
+      dma_to_lds16(vh + key * kHeadDim + (vslot(r, slot) << 3), lds_addr(&lds_v[st][r0 * kHeadDim]));
     }
   };
 
@@ -237,7 +224,7 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
       float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
-      mx = fmaxf(mx, pp_partner(mx, g));
+      mx = fmaxf(mx, partner_f(mx, g));
       const float mc = mx * sl2;
       const bool up = mine && (mc > m);
       const float alpha = up ? fast_exp2(m - mc) : 1.f;  // 0 on a row's first unit
@@ -314,7 +301,7 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
   __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
 
   // ---- epilogue ----
-  const float lt = l + pp_partner(l, g);
+  const float lt = l + partner_f(l, g);
   if (!qvalid) return;
   const float inv = 1.f / lt;
   u16* orow = a.out + ((int64_t)h * a.N + row) * kHeadDim;
@@ -334,8 +321,7 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
 }
 
 hipError_t launch_forward_pp(const FwdArgs& a, hipStream_t s) {
-  fwd_pp_kernel<<<a.total, 512, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(fwd_pp_kernel, dim3(a.total), dim3(512), s, a);
 }
 
 }  // namespace solattn

@@ -126,13 +126,6 @@ constexpr int kGDmaPerStage = 4;         // per wave: 2 token + 2 weight instruc
 
 __device__ __forceinline__ int g_chunk(int row, int c) { return c ^ ((row >> 2) & 3); }
 
-__device__ __forceinline__ void g_dma16(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gptr), "s"(lds)
-               : "memory", "m0");
-}
-
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
@@ -175,8 +168,8 @@ __global__ __launch_bounds__(512, 1) void fp8_gemm_kernel(Fp8GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r0 = (wave * 2 + i) * 16;
-      g_dma16(abase[i] + k0, lds_addr(&lds_a[st][r0 * kGK]));
-      g_dma16(wbase[i] + k0, lds_addr(&lds_w[st][r0 * kGK]));
+      dma_to_lds16(abase[i] + k0, lds_addr(&lds_a[st][r0 * kGK]));
+      dma_to_lds16(wbase[i] + k0, lds_addr(&lds_w[st][r0 * kGK]));
     }
   };
 
@@ -272,8 +265,7 @@ __global__ __launch_bounds__(512, 1) void fp8_gemm_kernel(Fp8GemmArgs a) {
 
 hipError_t launch_quantize_rows(const Fp8QuantArgs& a, hipStream_t s) {
   const int64_t blocks = (a.M + 3) / 4;
-  quantize_rows_kernel<<<(unsigned)blocks, 256, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(quantize_rows_kernel, dim3((unsigned)blocks), dim3(256), s, a);
 }
 
 hipError_t launch_fp8_gemm(const Fp8GemmArgs& a0, hipStream_t s) {
@@ -281,8 +273,7 @@ hipError_t launch_fp8_gemm(const Fp8GemmArgs& a0, hipStream_t s) {
   a.tiles_m = (a.M + kGT - 1) / kGT;
   a.tiles_n = (a.N + kGT - 1) / kGT;
   a.grid = (a.tiles_m * a.tiles_n + 7) & ~7;
-  fp8_gemm_kernel<<<a.grid, kGWaves * 64, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(fp8_gemm_kernel, dim3(a.grid), dim3(kGWaves * 64), s, a);
 }
 
 }  // namespace solattn

@@ -142,6 +142,16 @@ struct MergeArgs {
   int N, H;
 };
 
+// Launch of a one-argument kernel returning the status of this launch alone:
+// hipLaunchKernel reports the error of the launch it makes, where
+// hipGetLastError would also return (and clear) an earlier, unrelated error
+// of the calling thread.
+template <class A>
+inline hipError_t launch_kernel(void (*kernel)(A), dim3 grid, dim3 block, hipStream_t s, A arg) {
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, s);
+}
+
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 hipError_t launch_stats(const StatsArgs& a, hipStream_t s);
 hipError_t launch_moments(const MomentArgs& a, hipStream_t s);

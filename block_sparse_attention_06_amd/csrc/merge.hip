@@ -42,8 +42,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.H * a.N;
-  combine_kernel<<<(unsigned)((rows + kCombineRows - 1) / kCombineRows), 256, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(combine_kernel, dim3((unsigned)((rows + kCombineRows - 1) / kCombineRows)),
+                       dim3(256), s, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -82,8 +82,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   const int64_t threads = (int64_t)a.H * a.N * 16;
-  merge_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), s, a);
 }
 
 }  // namespace solattn

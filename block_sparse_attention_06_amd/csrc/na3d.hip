@@ -38,22 +38,9 @@ constexpr int kNWait = (((kNAhead - 1) * kNDma) & 15) | 0x0F70;
 static_assert((kNAhead - 1) * kNDma < 16, "vmcnt field");
 constexpr int kPR = 4, kPC = 8;          // query patch: rows x columns
 
-__device__ __forceinline__ int n_kslot(int row, int c) { return c ^ (row & 15); }
-__device__ __forceinline__ int n_vslot(int row, int c) { return c ^ ((row & 3) << 2); }
-
 __device__ __forceinline__ int win_start(int p, int len, int k) { return min(max(p - (k >> 1), 0), len - k); }
 
 constexpr float kSlackSum = 256.f;  // 2^8: the reference may lag the row maximum by 8 (log2 units)
-
-// Direct global -> LDS load of 16 bytes per lane from sbase + voff (sbase
-// wave-uniform, voff a 32-bit per-lane byte offset); lane l's bytes land at
-// LDS byte address lds + 16 l.  Ordered by explicit vmcnt waits and barriers.
-__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory", "m0");
-}
 
 }  // namespace
 
@@ -132,8 +119,8 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
   for (int i = 0; i < 2; ++i) {
     const int r = wave * 8 + i * 4 + (lane >> 4);
     const uint32_t key = (uint32_t)((r / UC) * X + min(xu + r % UC, X - 1));
-    koff[i] = key * (kHeadDim * 2) + (n_kslot(r, slot) << 4);
-    voff[i] = key * (kHeadDim * 2) + (n_vslot(r, slot) << 4);
+    koff[i] = key * (kHeadDim * 2) + (kslot(r, slot) << 4);
+    voff[i] = key * (kHeadDim * 2) + (vslot(r, slot) << 4);
   }
   const int ylast = Y - UR;  // last start of a row group that stays in the grid
   auto dma_unit = [&](int ff, int yy, int st) __attribute__((always_inline)) {
@@ -188,13 +175,13 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
   // add constants), formed once.
   uint32_t nkofs[8], nvofs[4];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) nkofs[ks] = (uint32_t)(r32 * kHeadDim + (n_kslot(r32, ks * 2 + g) << 3)) * 2u;
+  for (int ks = 0; ks < 8; ++ks) nkofs[ks] = (uint32_t)(r32 * kHeadDim + (kslot(r32, ks * 2 + g) << 3)) * 2u;
   {
     const int G = lane >> 4, j = lane & 15, r0 = g * 4 + (j >> 2);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const int col = dt * 32 + (G & 1) * 16 + 4 * (j & 3);
-      nvofs[dt] = (uint32_t)(r0 * kHeadDim + (n_vslot(r0, col >> 3) << 3) + (col & 7)) * 2u;
+      nvofs[dt] = (uint32_t)(r0 * kHeadDim + (vslot(r0, col >> 3) << 3) + (col & 7)) * 2u;
     }
   }
   // One unit; st = u mod kNRing.  The loop below is unrolled over one turn of
@@ -264,8 +251,7 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
 #pragma unroll
       for (int rr = 0; rr < UR; ++rr) mx = fmaxf(mx, mxr[rr] + rbias[rr]);
       // partner lane l ^ 32 holds the other 16 keys of the same query
-      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      const float mc = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * sl2;
+      const float mc = pair_max(mx) * sl2;
       const bool up = mc > m;
       const float alpha = up ? fast_exp2(m - mc) : 1.f;
       l *= alpha;
@@ -300,10 +286,8 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
   __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
 
   // epilogue: the query's denominator is split over lanes l and l ^ 32
-  const auto pl = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
-  const float lt = __uint_as_float(pl[0]) + __uint_as_float(pl[1]);
-  const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l32), __float_as_uint(l32), false, false);
-  const float lt32 = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+  const float lt = pair_sum(l);
+  const float lt32 = pair_sum(l32);
   if (!qvalid) return;
   const float inv = 1.f / lt;
   u16* orow = a.out + head + qrow * kHeadDim;
@@ -324,11 +308,8 @@ hipError_t launch_na3d(const Na3dArgs& a, hipStream_t s) {
   const int wgs = ((a.X + kPC - 1) / kPC) * ((a.Y + kPR - 1) / kPR) * ((a.T + 3) / 4) * a.H;
   // the patch's key columns (at most kPC - 1 + kx) fit in a 16-column unit
   // row (and the grid has the two rows of a unit)
-  if (kPC - 1 + a.kx <= 16 && a.Y >= 2)
-    na3d_kernel<2><<<wgs, 256, 0, s>>>(a);
-  else
-    na3d_kernel<1><<<wgs, 256, 0, s>>>(a);
-  return hipGetLastError();
+  if (kPC - 1 + a.kx <= 16 && a.Y >= 2) return launch_kernel(na3d_kernel<2>, dim3(wgs), dim3(256), s, a);
+  return launch_kernel(na3d_kernel<1>, dim3(wgs), dim3(256), s, a);
 }
 
 }  // namespace solattn

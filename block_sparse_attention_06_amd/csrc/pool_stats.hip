@@ -106,15 +106,11 @@ __global__ __launch_bounds__(256) void forms_kernel(PoolArgs a) {
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s) {
   dim3 grid(a.nb, a.H, 2);
-  if (a.B == 64)
-    pool_kernel<64><<<grid, 256, 0, s>>>(a);
-  else
-    pool_kernel<128><<<grid, 256, 0, s>>>(a);
-  if (hipError_t e = hipGetLastError()) return e;
-  if (a.khi) {  // the forward pass's forms (khi, klo and vsumT are set together)
-    forms_kernel<<<dim3(a.nb_pad / 16, a.H), 256, 0, s>>>(a);
-    return hipGetLastError();
-  }
+  const hipError_t e = a.B == 64 ? launch_kernel(pool_kernel<64>, grid, dim3(256), s, a)
+                                 : launch_kernel(pool_kernel<128>, grid, dim3(256), s, a);
+  if (e != hipSuccess) return e;
+  // the forward pass's forms (khi, klo and vsumT are set together)
+  if (a.khi) return launch_kernel(forms_kernel, dim3(a.nb_pad / 16, a.H), dim3(256), s, a);
   return hipSuccess;
 }
 
@@ -191,8 +187,7 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
 
 hipError_t launch_stats(const StatsArgs& a, hipStream_t s) {
   dim3 grid((a.N + kQTile - 1) / kQTile, a.H);
-  stats_kernel<<<grid, 256, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(stats_kernel, grid, dim3(256), s, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -349,10 +344,10 @@ __global__ __launch_bounds__(256) void moments_final_kernel(MomentArgs a) {
 }
 
 hipError_t launch_moments(const MomentArgs& a, hipStream_t s) {
-  moments_part_kernel<<<dim3(kHeadDim / 32, kMomentSplits, a.H), 256, 0, s>>>(a);
-  if (hipError_t e = hipGetLastError()) return e;
-  moments_final_kernel<<<dim3(kHeadDim / 16, a.H), 256, 0, s>>>(a);
-  return hipGetLastError();
+  const hipError_t e =
+      launch_kernel(moments_part_kernel, dim3(kHeadDim / 32, kMomentSplits, a.H), dim3(256), s, a);
+  if (e != hipSuccess) return e;
+  return launch_kernel(moments_final_kernel, dim3(kHeadDim / 16, a.H), dim3(256), s, a);
 }
 
 // stats_moment_kernel: one wave per 32 query rows, four per 128-row tile, and
@@ -453,8 +448,7 @@ __global__ __launch_bounds__(256, 3) void stats_moment_kernel(StatsMomentArgs a)
 
 hipError_t launch_stats_moment(const StatsMomentArgs& a, hipStream_t s) {
   dim3 grid((a.N + kMomentTiles * kQTile - 1) / (kMomentTiles * kQTile), a.H);
-  stats_moment_kernel<<<grid, 256, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(stats_moment_kernel, grid, dim3(256), s, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -482,8 +476,7 @@ __global__ __launch_bounds__(256) void proxy_kernel(ProxyArgs a) {
 
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s) {
   dim3 grid((a.nrows + kQTile - 1) / kQTile, a.H);
-  proxy_kernel<<<grid, 256, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(proxy_kernel, grid, dim3(256), s, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -549,10 +542,10 @@ __global__ __launch_bounds__(256) void mask_kernel(MaskArgs a) {
 }
 
 hipError_t launch_mask(const MaskArgs& a, hipStream_t s) {
-  zero_counts_kernel<<<1, 64, 0, s>>>(a.counts);
+  const hipError_t e = launch_kernel(zero_counts_kernel, dim3(1), dim3(64), s, a.counts);
+  if (e != hipSuccess) return e;
   dim3 grid((a.nrows + kQTile - 1) / kQTile, a.H);
-  mask_kernel<<<grid, 256, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel(mask_kernel, grid, dim3(256), s, a);
 }
 
 }  // namespace solattn

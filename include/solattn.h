@@ -37,8 +37,11 @@
  *     all work is enqueued on `stream` (a hipStream_t; NULL = null stream).
  *   - Softmax scale is 1/sqrt(d).  Only d = 128 is supported; B is 64 or 128.
  *   - Return codes: SOL_OK, or a negative SOL_ERR_*.  Arguments are checked
- *     before anything is enqueued; on an error nothing is launched.
- *     SOL_ERR_HIP reports a launch failure from the HIP runtime.
+ *     before anything is enqueued: SOL_ERR_INVALID_ARG and SOL_ERR_UNSUPPORTED
+ *     mean nothing was launched.  SOL_ERR_HIP reports the failure of one of
+ *     the call's own kernel launches (the status that launch returned, never
+ *     an earlier error pending on the thread); launches of the same call
+ *     that precede it stay enqueued, and the outputs are then undefined.
  *   - Stateless and thread-safe.  Calls on different streams that write
  *     disjoint outputs may overlap.
  *   - Offsets are 64-bit throughout (a 4K sequence of 130,686 tokens times 32
