@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--beta", type=float, default=0.5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true", help="skip beta=1.0 and dense 4K lines")
-    ap.add_argument("--cpu-seconds", type=float, default=18.0,
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run three plain 1 GiB device-to-device copies (reference "
@@ -103,6 +103,38 @@ def cpu_baseline(Q, K, V, B, beta, budget_s):
     }
 
 
+def cpu_full_calls(gpu_ms):
+    """The fp64 oracle (as is) on whole calls of the small workloads, timed on
+    the host beside the GPU: tiny (beta 0), stage-1 768x512 (beta 0.5) and one
+    head of the audio->video cross-attention (dense).  ``gpu_ms`` maps each
+    name to the GPU's ms/call of the same call (the cross head: a 32-head call
+    divided by 32)."""
+    import oracle as O
+    from synth import CROSS, WORKLOADS, clustered, cross_head
+    res = {}
+    for name, beta in (("tiny", 0.0), ("stage1", 0.5)):
+        w = WORKLOADS[name]
+        Q, K, V = clustered(w, threads=16)
+        t0 = time.perf_counter()
+        O.sol_attn_ref(Q, K, V, w.block, beta)
+        el = time.perf_counter() - t0
+        flops = 4.0 * w.heads * w.n * w.n * w.head_dim
+        res[f"{name}_beta{beta}"] = {
+            "oracle_ms_per_call": el * 1e3, "oracle_tflops_dense_equiv": flops / el / 1e12,
+            "gpu_ms_per_call": gpu_ms.get(name), "heads": w.heads, "tokens": w.n}
+    c = CROSS
+    q, k, v = cross_head(c["nq"], c["nk"], c["head_dim"], c["seed"], 0)
+    t0 = time.perf_counter()
+    O.dense_ref(q[None], k[None], v[None])
+    el = time.perf_counter() - t0
+    flops = 4.0 * c["nq"] * c["nk"] * c["head_dim"]
+    res["cross_one_head"] = {"oracle_ms_per_call": el * 1e3,
+                             "oracle_tflops_dense_equiv": flops / el / 1e12,
+                             "gpu_ms_per_head": gpu_ms.get("cross_head"),
+                             "queries": c["nq"], "keys": c["nk"]}
+    return res
+
+
 def fp8_projection(sa, torch, tokens, hidden, dev, stream, reps=5):
     """FP8 projection around attention at the 4K token count: per-row E4M3
     quantisation of bf16 activations [tokens, hidden], then the GEMM against
@@ -151,8 +183,10 @@ def workload_lines(sa, torch, name, to_dev, stream, reps=5):
     ws = torch.empty(max(1, sa.sol_attn_workspace_size(N, N, H, d, B, sa.SOL_SPARSE)),
                      dtype=torch.uint8, device=q.device)
     kb, _ = sa.sol_attn_pool(k, v, B)
-    mu, sigma = sa.sol_attn_row_stats(q, kb, B, N)
     nb = (N + B - 1) // B
+    # the statistics the call routes with (moment form from 128 blocks on)
+    stats = sa.sol_attn_row_stats_moment if nb >= 128 else sa.sol_attn_row_stats
+    mu, sigma = stats(q, kb, B, N)
     flops = 4.0 * H * N * N * d
     res = {"heads": H, "tokens": N, "block": B, "centres": w.centres, "seed": w.seed}
     for beta in w.betas:
@@ -390,6 +424,9 @@ def main():
     alg_flops = 4.0 * d * B * cnt[0]
     achieved = alg_flops / (fwd_ms * 1e-3) / 1e12
     executed = 4.0 * d * B * 32 * cnt[1] / (fwd_ms * 1e-3) / 1e12
+    # HBM bytes per launch of the fused kernel: calibrated rocprofv3
+    # FETCH_SIZE / WRITE_SIZE counters of the same kernel source (null once the
+    # source has changed since the counters were taken)
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         try:
@@ -399,7 +436,25 @@ def main():
         except Exception:
             traffic = None
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic}
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "traffic_source": os.path.relpath(TRAFFIC_FILE, ROOT) if traffic else None,
+                "work": "4 d B flop per selected (row, block) pair",
+                "executed_tile_tflops": executed,
+                "executed_tile_frac": executed / PEAK_BF16_TFLOPS,
+                "executed_work": "4 d 32 B flop per (32-row tile, block) pair with a selection"}
+
+    # routing kernels against the HBM roof: pool reads K and V once and writes
+    # the fp32 means; the moment-form statistics read Q once (plus the pooled
+    # keys for the moments) and write mu and sigma
+    pool_bytes = 2.0 * H * N * d * 2 + 2.0 * H * nb * d * 4
+    stats_bytes = 1.0 * H * N * d * 2 + H * nb * d * 4 + 2.0 * H * N * 4
+    hbm = {
+        "pool": {"ms": pool_ms, "bytes": pool_bytes, "gbs": pool_bytes / pool_ms / 1e6,
+                 "frac": pool_bytes / pool_ms / 1e6 / PEAK_HBM_GBS},
+        "row_stats_moment": {"ms": stats_ms, "bytes": stats_bytes,
+                             "gbs": stats_bytes / stats_ms / 1e6,
+                             "frac": stats_bytes / stats_ms / 1e6 / PEAK_HBM_GBS},
+    }
 
     extras = {}
     if not args.no_extras:
@@ -429,7 +484,8 @@ def main():
         extras["4k_sparse_kv_sharded"] = kv_sharded(sa, torch, q, k, v, B, args.beta, stream,
                                                     dense_flops, call_ms)
         extras["fp8_projection_4k"] = fp8_projection(sa, torch, N, H * d, q.device, stream)
-        log("stage-1 and stage-2 workloads")
+        log("tiny, stage-1 and stage-2 workloads")
+        extras["tiny"] = workload_lines(sa, torch, "tiny", to_dev, stream, reps=20)
         extras["stage1_768x512"] = workload_lines(sa, torch, "stage1", to_dev, stream)
         extras["stage2_1536x1024"] = workload_lines(sa, torch, "stage2", to_dev, stream)
         extras["na3d_decoder_tile_4k"] = na3d_decoder_tile(sa, torch, q.device, stream)
@@ -438,6 +494,12 @@ def main():
     if not args.no_cpu:
         log("cpu oracle baseline")
         cpu = cpu_baseline(Q, K, V, B, args.beta, args.cpu_seconds)
+        gpu_ms = {"cross_head": float(np.mean(cross_ms)) / H}
+        if "tiny" in extras:
+            gpu_ms["tiny"] = extras["tiny"]["beta_0.0"]["ms_per_call"]
+            gpu_ms["stage1"] = extras["stage1_768x512"]["beta_0.5"]["ms_per_call"]
+        log("cpu oracle full calls (tiny, stage-1, one cross-attention head)")
+        cpu["full_calls"] = cpu_full_calls(gpu_ms)
 
     rec = {
         "metric": METRIC,
@@ -448,7 +510,6 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": step_ms,
         "higher_is_better": True,
-        "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
@@ -465,10 +526,11 @@ def main():
         "ms_per_call_4k_sparse_min": float(np.min(self_ms)),
         "dense_equiv_tflops_4k_sparse": call_tflops,
         "pct_bf16_peak_4k_sparse": 100 * call_tflops / PEAK_BF16_TFLOPS,
-        "components_ms": {"pool": pool_ms, "row_stats": stats_ms, "fused_forward": fwd_ms,
+        "components_ms": {"pool": pool_ms, "row_stats": stats_ms,
+                          "fused_forward_with_forms": fwd_ms,
                           "cross_attention_halves_plus_merge": float(np.mean(cross_ms))},
         "density": {"rho_row": rho_row, "rho_tile32": rho_tile32, "rho_tile128": rho_tile128},
-        "executed_tile_tflops": executed,
+        "routing_hbm": hbm,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extras": extras,

@@ -17,7 +17,7 @@ import block_sparse_attention_06_amd as sa  # noqa: E402
 import oracle as O  # noqa: E402
 from synth import clustered, clustered_head, gaussian, WORKLOADS  # noqa: E402
 from tests.parity_utils import (best_match, check_close, dev, host, mask_mismatch_ok,  # noqa: E402
-                                sparse_with_ties)
+                                sparse_with_ties, tiles_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,6 +26,15 @@ INF = float("inf")
 
 def _head(bits, h):
     return O.bf16_to_f64(bits[h])
+
+
+def _clustered_small(H, N, B, seed=70):
+    """Clustered recipe (one centre per key block, one per query block) at a
+    given shape; heads 0..H-1."""
+    from synth import Workload
+    nb = (N + B - 1) // B
+    w = Workload("custom", H, N, 0, 128, B, nb, 0.5, seed, (0.5,))
+    return clustered(w)
 
 
 # ---------------------------------------------------------------------------
@@ -70,23 +79,56 @@ def test_proxy_and_stats_parity(case):
         assert np.abs(host(sigma[h]) - sr).max() < 2e-5
 
 
-@pytest.mark.parametrize("H,N,B", [(2, 2048, 64), (2, 1500, 128), (2, 20000, 128), (1, 130, 64)])
+@pytest.mark.parametrize("H,N,B", [(2, 2048, 64), (2, 1500, 128), (2, 20000, 128), (1, 130, 64),
+                                   (2, 130686, 128), (1, 130686, 64)])
 def test_row_stats_moment_parity(H, N, B):
     """Moment form (mean and covariance of the pooled keys) against the oracle's
-    statistics of the proxy scores, and against the direct form on the GPU."""
-    Q, K, V = gaussian(H, N, 128, seed=60 + N)
+    statistics of the proxy scores, and against the direct form on the GPU.
+    The last two shapes have the 4K workload's block counts (1021 blocks of
+    128, 2042 of 64, the last one ragged); there the oracle checks whole
+    first, middle and last 128-row tiles."""
+    Q, K, V = gaussian(H, N, 128, seed=60 + N + B)
     q = dev(Q)
     kbar, _ = sa.sol_attn_pool(dev(K), dev(V), B)
     mu, sigma = sa.sol_attn_row_stats_moment(q, kbar, B, N)
     mu_d, sigma_d = sa.sol_attn_row_stats(q, kbar, B, N)
     torch.cuda.synchronize()
+    rows = np.arange(N) if N <= 20000 else tiles_rows(N)
     for h in range(H):
         kb = O.pool_ref(_head(K, h), B)
-        mr, sr = O.row_stats_ref(O.proxy_ref(_head(Q, h), kb))
-        assert np.abs(host(mu[h]) - mr).max() < 2e-5
-        assert np.abs(host(sigma[h]) - sr).max() < 2e-5
+        mr, sr = O.row_stats_ref(O.proxy_ref(_head(Q, h)[rows], kb))
+        assert np.abs(host(mu[h])[rows] - mr).max() < 2e-5
+        assert np.abs(host(sigma[h])[rows] - sr).max() < 2e-5
     assert (mu - mu_d).abs().max().item() < 4e-5
     assert (sigma - sigma_d).abs().max().item() < 4e-5
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5, 1.0])
+def test_block_mask_parity_moment_form(beta):
+    """157 key blocks (ragged last one): the forward call routes with the
+    moment-form statistics from 128 blocks on, so the mask is built from
+    those, with the forward kernel's own proxy and predicate, and compared
+    with the oracle's selection outside the near-tie band."""
+    H, N, B = 2, 20000, 128
+    Q, K, V = _clustered_small(H, N, B)
+    q = dev(Q)
+    kbar, _ = sa.sol_attn_pool(dev(K), dev(V), B)
+    mu, sigma = sa.sol_attn_row_stats_moment(q, kbar, B, N)
+    rows = tiles_rows(N)
+    masks = []
+    for t0 in sorted(set((rows // 128) * 128)):
+        m, _ = sa.sol_attn_block_mask(q, kbar, mu, sigma, beta, B, N, row0=int(t0),
+                                      nrows=min(128, N - int(t0)))
+        masks.append(m.cpu().numpy())
+    torch.cuda.synchronize()
+    for h in range(H):
+        kb = O.pool_ref(_head(K, h), B)
+        p = O.proxy_ref(_head(Q, h)[rows], kb)
+        mr, sr = O.row_stats_ref(p)
+        info = dict(p=p, mu=mr, sigma=sr, mask=O.select_ref(p, mr, sr, beta))
+        gm = np.concatenate([m[h] for m in masks])
+        ok, n = mask_mismatch_ok(gm, info, beta)
+        assert ok, f"head {h}: {n} mask mismatches outside the near-tie band"
 
 
 @pytest.mark.parametrize("beta", [0.0, 0.5, 1.0, -0.5])

@@ -44,7 +44,11 @@ def _check_sampled(name, beta, heads):
     masks = {}
     if mode == sa.SOL_SPARSE:
         kbar, _ = sa.sol_attn_pool(k, v, B)
-        mu, sigma = sa.sol_attn_row_stats(q, kbar, B, N)
+        # the statistics the call routes with: moment form from 128 blocks on
+        if (N + B - 1) // B >= 128:
+            mu, sigma = sa.sol_attn_row_stats_moment(q, kbar, B, N)
+        else:
+            mu, sigma = sa.sol_attn_row_stats(q, kbar, B, N)
         for t0 in sorted(set((rows // 128) * 128)):
             nr = min(128, N - t0)
             m, _ = sa.sol_attn_block_mask(q, kbar, mu, sigma, beta, B, N, row0=int(t0), nrows=nr)
