@@ -29,6 +29,7 @@ __all__ = [
     "sol_attn_row_stats",
     "sol_attn_row_stats_moment",
     "sol_attn_forward",
+    "sol_attn_forward_noalloc",
     "sol_attn_workspace_size",
     "attn_lse_merge",
     "sol_attn_error_string",
@@ -81,6 +82,7 @@ def load_library() -> ctypes.CDLL:
         "sol_attn_row_stats": (I, [P, P, P, P, I, I, I, I, I, P]),
         "sol_attn_row_stats_moment": (I, [P, P, P, P, I, I, I, I, I, P, S, P]),
         "sol_attn_forward": (I, [P, P, P, P, P, I, I, I, I, F, I, I, P, S, P]),
+        "sol_attn_forward_noalloc": (I, [P, P, P, P, P, I, I, I, I, F, I, I, P]),
         "sol_attn_workspace_size": (S, [I, I, I, I, I, I]),
         "attn_lse_merge": (I, [P, P, P, P, P, P, I, I, I, P]),
         "sol_attn_error_string": (Z, [I]),
@@ -239,6 +241,32 @@ def sol_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, B: int =
     _check("sol_attn_forward", lib.sol_attn_forward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), N, H, d, int(B), float(beta),
         int(mode), Nk, _ptr(workspace), have, _stream(stream)))
+    return out, lse
+
+
+def sol_attn_forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                             out: torch.Tensor, lse: Optional[torch.Tensor] = None, B: int = 128,
+                             beta: float = 0.5, mode: int = SOL_SPARSE, stream=None):
+    """:func:`sol_attn_forward` for callers that cannot allocate: no workspace
+    (the library's own per-GPU scratch, at most 128 MiB, is used) and no
+    output allocated here -- ``out`` (and ``lse``, if wanted) must be given.
+    Calls that overlap in time on one GPU share that scratch and race."""
+    lib = load_library()
+    _want(q, "q", torch.bfloat16, 3)
+    _want(k, "k", torch.bfloat16, 3)
+    _want(v, "v", torch.bfloat16, 3)
+    H, N, d = q.shape
+    Nk = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != H or k.shape[2] != d:
+        raise ValueError("k and v must be [H, Nk, d] with q's H and d")
+    _want_shape(out, "out", torch.bfloat16, (H, N, d))
+    if lse is not None:
+        _want_shape(lse, "lse", torch.float32, (H, N))
+    if math.isnan(beta):
+        raise ValueError("beta must not be NaN")
+    _check("sol_attn_forward_noalloc", lib.sol_attn_forward_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), N, H, d, int(B), float(beta), int(mode),
+        Nk, _stream(stream)))
     return out, lse
 
 

@@ -2,6 +2,7 @@
 // workspace layout, split planning and kernel launches on the caller's stream.
 // Nothing here allocates, frees or synchronises.
 #include <math.h>
+#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -9,6 +10,14 @@
 #include "launch.hpp"
 
 using namespace solattn;
+
+// Device scratch of the allocation-free forward entry point: a file-scope
+// array, one copy per GPU the library runs on, held until the process ends.
+// Host code never uses the array's name as an address (on the host it is only
+// a stand-in for the symbol): the device address of each GPU's copy comes from
+// hipGetSymbolAddress with that GPU current, once per device, and is kept.
+static constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -153,6 +162,106 @@ int check_shape(int N, int H, int d) {
 
 int check_block(int B) { return (B == 64 || B == 128) ? SOL_OK : SOL_ERR_UNSUPPORTED; }
 
+// Argument checks of the forward call (Nk = 0 already replaced by N).
+int check_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* out,
+                  int N, int H, int d, int B, float beta, int mode, int Nk) {
+  if (!q || !k || !v || !out) return SOL_ERR_INVALID_ARG;
+  if (Nk < 0) return SOL_ERR_INVALID_ARG;
+  if (int r = check_shape(N, H, d)) return r;
+  if (mode != SOL_DENSE && mode != SOL_SPARSE) return SOL_ERR_UNSUPPORTED;
+  if (mode == SOL_SPARSE) {
+    if (int r = check_block(B)) return r;
+    if (isnan(beta)) return SOL_ERR_INVALID_ARG;
+  }
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return SOL_ERR_INVALID_ARG;
+  return SOL_OK;
+}
+
+// Launches of the forward call on a checked, large enough workspace.
+int forward_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                   float* lse, int N, int H, int B, float beta, int mode, int Nk, const Plan& p,
+                   void* workspace, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const bool sparse = mode == SOL_SPARSE && !(isinf(beta) && beta < 0);
+  const Split& sp = sparse ? p.sp : p.dn;
+
+  FwdArgs f{};
+  f.q = q; f.k = k; f.v = v; f.out = out; f.lse = lse;
+  f.beta = beta; f.N = N; f.Nk = Nk; f.H = H;
+  f.nb = sp.nb; f.nb_pad = sp.nb_pad;
+  f.n_qt = cdiv(N, 128);
+  f.splits = sp.splits; f.tiles_per_split = sp.tiles_per_split;
+  f.total = H * f.n_qt * f.splits;
+  if (sparse) {
+    PoolArgs pa{k, v, (float*)(ws + p.off_kbar), (float*)(ws + p.off_vbar),
+                (uint16_t*)(ws + p.off_vsum), (uint16_t*)(ws + p.off_khi),
+                (uint16_t*)(ws + p.off_klo), Nk, H, B, sp.nb, sp.nb_pad};
+    if (int r = hip_status(launch_pool(pa, s))) return r;
+    float* mu = (float*)(ws + p.off_mu);
+    float* sigma = (float*)(ws + p.off_sigma);
+    if (p.moments) {
+      MomentArgs ma{pa.kbar, (uint16_t*)(ws + p.off_chi), (uint16_t*)(ws + p.off_clo),
+                    (float*)(ws + p.off_mbar), (float*)(ws + p.off_mpart), H, sp.nb};
+      if (int r = hip_status(launch_moments(ma, s))) return r;
+      StatsMomentArgs sm{q, ma.chi, ma.clo, ma.mbar, mu, sigma, N, H};
+      if (int r = hip_status(launch_stats_moment(sm, s))) return r;
+    } else {
+      StatsArgs sa{q, pa.kbar, mu, sigma, N, H, sp.nb};
+      if (int r = hip_status(launch_stats(sa, s))) return r;
+    }
+    f.khi = pa.khi; f.klo = pa.klo; f.vsumT = pa.vsumT; f.mu = mu; f.sigma = sigma;
+  }
+  if (f.splits > 1) {
+    f.part_o = (float*)(ws + p.off_po);
+    f.part_ml = (float*)(ws + p.off_pml);
+  }
+  // Dense attention over long sequences (no key split) runs the 8-wave
+  // ping-pong kernel on 256-row tiles; sparse attention, dense short query
+  // sets and split keys the pipelined 4-wave kernel.
+  const long long pp_wgs = (long long)H * cdiv(N, 256);
+  const bool use_pp = !sparse && f.splits == 1 && pp_wgs >= kCUs;
+  if (use_pp) {
+    FwdArgs fp = f;
+    fp.total = (int)pp_wgs;
+    if (int r = hip_status(launch_forward_pp(fp, s))) return r;
+  } else {
+    if (int r = hip_status(launch_forward(f, sparse, sparse ? B : 128, s))) return r;
+  }
+  if (f.splits > 1) {
+    CombineArgs c{f.part_o, f.part_ml, out, lse, N, H, f.splits};
+    if (int r = hip_status(launch_combine(c, s))) return r;
+  }
+  return SOL_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device that runs `stream` (the current device
+// for the null stream).
+int scratch_of_stream_device(void* stream, void** out) {
+  int cur = 0, dev = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return SOL_ERR_HIP;
+  dev = cur;
+  if (stream && hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) return SOL_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SOL_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return SOL_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return SOL_ERR_HIP;
+    if (e != hipSuccess || !ptr) return SOL_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SOL_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -163,6 +272,8 @@ const char* sol_attn_error_string(int code) {
     case SOL_ERR_INVALID_ARG: return "invalid argument (null pointer, size, NaN beta, workspace or alignment)";
     case SOL_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 128, block 64 or 128, mode 0 or 1)";
     case SOL_ERR_HIP: return "HIP runtime reported a launch error";
+    case SOL_ERR_SCRATCH:
+      return "the call needs more scratch than the allocation-free entry point holds (128 MiB)";
     default: return "unknown error code";
   }
 }
@@ -256,72 +367,26 @@ size_t sol_attn_workspace_size(int N, int Nk, int H, int d, int B, int mode) {
 int sol_attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
                      float* lse, int N, int H, int d, int B, float beta, int mode, int Nk,
                      void* workspace, size_t ws_bytes, void* stream) {
-  if (!q || !k || !v || !out) return SOL_ERR_INVALID_ARG;
   if (Nk == 0) Nk = N;
-  if (Nk < 0) return SOL_ERR_INVALID_ARG;
-  if (int r = check_shape(N, H, d)) return r;
-  if (mode != SOL_DENSE && mode != SOL_SPARSE) return SOL_ERR_UNSUPPORTED;
-  if (mode == SOL_SPARSE) {
-    if (int r = check_block(B)) return r;
-    if (isnan(beta)) return SOL_ERR_INVALID_ARG;
-  }
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
-    return SOL_ERR_INVALID_ARG;
+  if (int r = check_forward(q, k, v, out, N, H, d, B, beta, mode, Nk)) return r;
   const Plan p = make_plan(N, Nk, H, B, mode);
   if (p.bytes > 0 && (!workspace || ws_bytes < p.bytes || !aligned(workspace, 256)))
     return SOL_ERR_INVALID_ARG;
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  const bool sparse = mode == SOL_SPARSE && !(isinf(beta) && beta < 0);
-  const Split& sp = sparse ? p.sp : p.dn;
+  return forward_launch(q, k, v, out, lse, N, H, B, beta, mode, Nk, p, workspace, stream);
+}
 
-  FwdArgs f{};
-  f.q = q; f.k = k; f.v = v; f.out = out; f.lse = lse;
-  f.beta = beta; f.N = N; f.Nk = Nk; f.H = H;
-  f.nb = sp.nb; f.nb_pad = sp.nb_pad;
-  f.n_qt = cdiv(N, 128);
-  f.splits = sp.splits; f.tiles_per_split = sp.tiles_per_split;
-  f.total = H * f.n_qt * f.splits;
-  if (sparse) {
-    PoolArgs pa{k, v, (float*)(ws + p.off_kbar), (float*)(ws + p.off_vbar),
-                (uint16_t*)(ws + p.off_vsum), (uint16_t*)(ws + p.off_khi),
-                (uint16_t*)(ws + p.off_klo), Nk, H, B, sp.nb, sp.nb_pad};
-    if (int r = hip_status(launch_pool(pa, s))) return r;
-    float* mu = (float*)(ws + p.off_mu);
-    float* sigma = (float*)(ws + p.off_sigma);
-    if (p.moments) {
-      MomentArgs ma{pa.kbar, (uint16_t*)(ws + p.off_chi), (uint16_t*)(ws + p.off_clo),
-                    (float*)(ws + p.off_mbar), (float*)(ws + p.off_mpart), H, sp.nb};
-      if (int r = hip_status(launch_moments(ma, s))) return r;
-      StatsMomentArgs sm{q, ma.chi, ma.clo, ma.mbar, mu, sigma, N, H};
-      if (int r = hip_status(launch_stats_moment(sm, s))) return r;
-    } else {
-      StatsArgs sa{q, pa.kbar, mu, sigma, N, H, sp.nb};
-      if (int r = hip_status(launch_stats(sa, s))) return r;
-    }
-    f.khi = pa.khi; f.klo = pa.klo; f.vsumT = pa.vsumT; f.mu = mu; f.sigma = sigma;
+int sol_attn_forward_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             uint16_t* out, float* lse, int N, int H, int d, int B, float beta,
+                             int mode, int Nk, void* stream) {
+  if (Nk == 0) Nk = N;
+  if (int r = check_forward(q, k, v, out, N, H, d, B, beta, mode, Nk)) return r;
+  const Plan p = make_plan(N, Nk, H, B, mode);
+  if (p.bytes > kScratchBytes) return SOL_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (p.bytes > 0) {
+    if (int r = scratch_of_stream_device(stream, &ws)) return r;
   }
-  if (f.splits > 1) {
-    f.part_o = (float*)(ws + p.off_po);
-    f.part_ml = (float*)(ws + p.off_pml);
-  }
-  // Dense attention over long sequences (no key split) runs the 8-wave
-  // ping-pong kernel on 256-row tiles; sparse attention, dense short query
-  // sets and split keys the pipelined 4-wave kernel.
-  const long long pp_wgs = (long long)H * cdiv(N, 256);
-  const bool use_pp = !sparse && f.splits == 1 && pp_wgs >= kCUs;
-  if (use_pp) {
-    FwdArgs fp = f;
-    fp.total = (int)pp_wgs;
-    if (int r = hip_status(launch_forward_pp(fp, s))) return r;
-  } else {
-    if (int r = hip_status(launch_forward(f, sparse, sparse ? B : 128, s))) return r;
-  }
-  if (f.splits > 1) {
-    CombineArgs c{f.part_o, f.part_ml, out, lse, N, H, f.splits};
-    if (int r = hip_status(launch_combine(c, s))) return r;
-  }
-  return SOL_OK;
+  return forward_launch(q, k, v, out, lse, N, H, B, beta, mode, Nk, p, ws, stream);
 }
 
 size_t sol_attn_shard_workspace_size(int N, int Nk, int nb_all, int H, int d, int B,

@@ -68,6 +68,7 @@ extern "C" {
 #define SOL_ERR_INVALID_ARG (-1) /* null pointer, size <= 0, NaN beta, short workspace, misalignment */
 #define SOL_ERR_UNSUPPORTED (-2) /* d != 128, B not in {64, 128}, unknown mode */
 #define SOL_ERR_HIP (-3)         /* the HIP runtime reported a launch error */
+#define SOL_ERR_SCRATCH (-4)     /* sol_attn_forward_noalloc: the call needs more than its scratch */
 
 /* modes of sol_attn_forward */
 #define SOL_DENSE 0  /* plain softmax attention; beta and B are ignored */
@@ -147,6 +148,28 @@ int sol_attn_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 
 /* Bytes of workspace sol_attn_forward needs for these sizes (0 if none). */
 size_t sol_attn_workspace_size(int N, int Nk, int H, int d, int B, int mode);
+
+/*
+ * sol_attn_forward without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, checks, kernels and
+ * results as sol_attn_forward, minus workspace and ws_bytes: the work space
+ * is a 128 MiB array inside the library, one per GPU, held from the library's
+ * load until the process ends (it covers the 4K latent workload:
+ * sol_attn_workspace_size(130686, 0, 32, 128, 128, SOL_SPARSE) is 106 MiB).
+ * The caller still passes q, k, v, out and lse.  No allocation or free is
+ * made.  The array of the GPU that runs `stream` is used (on its first use
+ * per GPU the library looks its address up once and keeps it).
+ * Returns SOL_ERR_SCRATCH, before any launch, when
+ * sol_attn_workspace_size(N, Nk, H, d, B, mode) exceeds 128 MiB.
+ * All calls on one GPU share its array: two calls that overlap in time on
+ * one GPU (different streams, or graph replays in flight) race and give
+ * undefined results; calls that follow each other on a stream are safe.  No
+ * array contents need clearing: every call writes all it reads.
+ */
+int sol_attn_forward_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             uint16_t* out, float* lse, int N, int H, int d, int B, float beta,
+                             int mode, int Nk, void* stream);
 
 /*
  * Exact merge of two partial answers over disjoint key sets.

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_error_strings(lib):
-    for code in (0, -1, -2, -3, 7):
+    for code in (0, -1, -2, -3, -4, 7):
         assert len(lib.sol_attn_error_string(code)) > 0
 
 
@@ -143,3 +143,23 @@ def test_workspace_sizes(lib):
     # short query against long keys: split partials
     assert ws(126, 130560, 32, 128, 128, 0) > 0
     assert ws(0, 10, 1, 128, 64, 1) == 0
+
+
+def test_noalloc_argument_errors(lib):
+    """The allocation-free forward checks its arguments like sol_attn_forward,
+    then refuses a call needing more than its 128 MiB scratch -- all before
+    any HIP call, so it runs without a GPU."""
+    f = lib.sol_attn_forward_noalloc
+    N = None
+    assert f(N, FAKE, FAKE, FAKE, N, 64, 1, 128, 64, 0.0, 1, 0, N) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, N, 0, 1, 128, 64, 0.0, 1, 0, N) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, N, 64, 1, 64, 64, 0.0, 1, 0, N) == -2
+    assert f(FAKE, FAKE, FAKE, FAKE, N, 64, 1, 128, 32, 0.0, 1, 0, N) == -2
+    assert f(FAKE, FAKE, FAKE, FAKE, N, 64, 1, 128, 64, math.nan, 1, 0, N) == -1
+    assert f(ctypes.c_void_p(0x10002), FAKE, FAKE, FAKE, N, 64, 1, 128, 64, 0.0, 1, 0, N) == -1
+    # 64 heads x 140,000 tokens needs ~226 MiB of workspace
+    assert lib.sol_attn_workspace_size(140000, 0, 64, 128, 128, 1) > 128 << 20
+    assert f(FAKE, FAKE, FAKE, FAKE, N, 140000, 64, 128, 128, 0.5, 1, 0, N) == -4
+    assert len(lib.sol_attn_error_string(-4)) > 0
+    # the 4K latent workload fits
+    assert lib.sol_attn_workspace_size(130686, 0, 32, 128, 128, 1) <= 128 << 20
