@@ -181,7 +181,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   // ---- online softmax of one unit's S tile.  Keys past the end are masked
   // first.  The tail forms the probabilities as the bf16 B operand of the PV
   // product (keys permuted within 16 as the accumulator layout holds them)
-  // and returns their row sum.  The head, taken only when the probabilities
+  // and returns their row sum, taken over the fp32 values before rounding:
+  // that sum is the denominator of both the output and lse (a sum of the
+  // rounded values would carry their rounding into lse unaveraged where a few
+  // keys hold the mass).  The head, taken only when the probabilities
   // against the current reference overran it, finds the row max and moves
   // the reference (m, with o and l rescaled); it returns the exponent offset
   // (-m, or -inf for rows that did not select the unit: p = 0).
@@ -214,31 +217,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     return mine ? -m : -__builtin_inff();
   };
   auto softmax_tail = [&](const f32x16& s, float neg_ref, bf16x8 (&pb)[2]) __attribute__((always_inline)) -> float {
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      pb[i >> 3][i & 7] = (__bf16)fast_exp2(__builtin_fmaf(s[i], sl2, neg_ref));
-    // Row sum of the bf16 probabilities (the values the PV product uses), two
-    // per instruction: dot(p_pair, (1, 1)) accumulated in fp32.
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bf16x2 p0 = {pb[0][2 * e], pb[0][2 * e + 1]};
-      const bf16x2 p1 = {pb[1][2 * e], pb[1][2 * e + 1]};
-      rs0 = __builtin_amdgcn_fdot2_f32_bf16(p0, one2, rs0, false);
-      rs1 = __builtin_amdgcn_fdot2_f32_bf16(p1, one2, rs1, false);
+    for (int i = 0; i < 16; ++i) {
+      const float e = fast_exp2(__builtin_fmaf(s[i], sl2, neg_ref));
+      pb[i >> 3][i & 7] = (__bf16)e;
+      if (i & 8) rs1 += e; else rs0 += e;
     }
     return rs0 + rs1;
   };
 
   // ---- the softmax tail of one unit interleaved with the S products of the
   // next: product k, then the probabilities of elements 2k and 2k+1 (scale,
-  // exponential, bf16 pair, pair row sum), fenced so that the compiler keeps
+  // exponential, bf16 pair, fp32 row sum), fenced so that the compiler keeps
   // the order; K operand reads run four products ahead.
   auto tail_and_s = [&](const f32x16& s_in, float neg_ref, bf16x8 (&pb)[2], int st, float& rsum) __attribute__((always_inline)) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
     u32x4 kf[8];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) kf[ks] = kop(st, ks);
@@ -251,11 +244,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       const float e0 = fast_exp2(__builtin_fmaf(s_in[2 * k], sl2, neg_ref));
       const float e1 = fast_exp2(__builtin_fmaf(s_in[2 * k + 1], sl2, neg_ref));
-      const __bf16 b0 = (__bf16)e0, b1 = (__bf16)e1;
-      pb[k >> 2][(2 * k) & 7] = b0;
-      pb[k >> 2][(2 * k + 1) & 7] = b1;
-      const bf16x2 pr = {b0, b1};
-      rs[k >> 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rs[k >> 2], false);
+      pb[k >> 2][(2 * k) & 7] = (__bf16)e0;
+      pb[k >> 2][(2 * k + 1) & 7] = (__bf16)e1;
+      rs[k >> 2] += e0 + e1;
       __builtin_amdgcn_sched_barrier(0);
     }
     rsum = rs[0] + rs[1];

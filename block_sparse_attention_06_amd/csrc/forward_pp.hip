@@ -191,22 +191,18 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
   // bounds each probability).  Otherwise -- always on a row's first unit,
   // whose reference is still -inf, and rarely after -- each selected row's
   // reference moves to its maximum (the accumulator is rescaled by phase A,
-  // before it adds this unit) and the probabilities are formed again.
+  // before it adds this unit) and the probabilities are formed again.  The
+  // row sum is taken over the fp32 probabilities before their rounding to
+  // bf16; it is the denominator of the output and of lse.
   auto probs = [&](float neg_ref) __attribute__((always_inline)) -> float {
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        pb[kt * 2 + (i >> 3)][i & 7] = (__bf16)fast_exp2(__builtin_fmaf(s[kt][i], sl2, neg_ref));
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16x2 pr = {pb[t][2 * e], pb[t][2 * e + 1]};
-        rsum[e] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rsum[e], false);
+      for (int i = 0; i < 16; ++i) {
+        const float e = fast_exp2(__builtin_fmaf(s[kt][i], sl2, neg_ref));
+        pb[kt * 2 + (i >> 3)][i & 7] = (__bf16)e;
+        rsum[i & 3] += e;
       }
     return (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
   };
