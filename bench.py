@@ -170,13 +170,14 @@ def fp8_projection(sa, torch, tokens, hidden, dev, stream, reps=5):
             "pct_fp8_peak": 100 * flops / g_ms / 1e9 / PEAK_FP8_TFLOPS}
 
 
-def workload_lines(sa, torch, name, to_dev, stream, reps=5):
+def workload_lines(sa, torch, name, to_dev, stream, reps=5, per_token=False):
     """ms/call, dense-equivalent TFLOP/s and achieved densities of one of the
-    smaller latent workloads (same clustered generator), per beta."""
+    smaller latent workloads (same clustered generator), per beta; with
+    ``per_token`` the generator's stress variant (one query centre per token)."""
     from synth import WORKLOADS, clustered
     w = WORKLOADS[name]
     H, N, d, B = w.heads, w.n, w.head_dim, w.block
-    Q, K, V = clustered(w, threads=16)
+    Q, K, V = clustered(w, threads=16, per_token=per_token)
     q, k, v = to_dev(Q), to_dev(K), to_dev(V)
     out = torch.empty_like(q)
     lse = torch.empty((H, N), dtype=torch.float32, device=q.device)
@@ -188,7 +189,8 @@ def workload_lines(sa, torch, name, to_dev, stream, reps=5):
     stats = sa.sol_attn_row_stats_moment if nb >= 128 else sa.sol_attn_row_stats
     mu, sigma = stats(q, kb, B, N)
     flops = 4.0 * H * N * N * d
-    res = {"heads": H, "tokens": N, "block": B, "centres": w.centres, "seed": w.seed}
+    res = {"heads": H, "tokens": N, "block": B, "centres": w.centres, "seed": w.seed,
+           "query_centres": "per token" if per_token else "per query block"}
     for beta in w.betas:
         mode = sa.SOL_DENSE if beta == float("-inf") else sa.SOL_SPARSE
         call = lambda: sa.sol_attn_forward(q, k, v, B=B, beta=beta, mode=mode, workspace=ws,
@@ -488,6 +490,8 @@ def main():
         extras["tiny"] = workload_lines(sa, torch, "tiny", to_dev, stream, reps=20)
         extras["stage1_768x512"] = workload_lines(sa, torch, "stage1", to_dev, stream)
         extras["stage2_1536x1024"] = workload_lines(sa, torch, "stage2", to_dev, stream)
+        extras["stage2_per_token_stress"] = workload_lines(sa, torch, "stage2", to_dev, stream,
+                                                           per_token=True)
         extras["na3d_decoder_tile_4k"] = na3d_decoder_tile(sa, torch, q.device, stream)
 
     cpu = None

@@ -20,6 +20,10 @@ drawn in this order, in float32:
 4. query token ``t``: ``q_t = c_{u_{t // B}} + noise * N(0, I_d)``;
 5. ``v_t`` ~ N(0, I_d).
 
+Per-token stress variant (``per_token=True``): step 3 draws one centre index
+per query token instead of per query block, so neighbouring rows share no
+centre and almost every query tile needs almost every key block.
+
 Cross-attention recipe (short audio query against long video keys): per head,
 Q, K, V ~ N(0, 1) drawn in that order.
 
@@ -106,21 +110,26 @@ def _head_rng(seed: int, h: int) -> np.random.Generator:
 
 
 def clustered_head(n: int, d: int, block: int, centres: int, noise: float,
-                   seed: int, h: int):
-    """bf16 bits of (q, k, v), each ``[n, d]``, for head ``h`` of the clustered recipe."""
+                   seed: int, h: int, per_token: bool = False):
+    """bf16 bits of (q, k, v), each ``[n, d]``, for head ``h`` of the clustered recipe
+    (``per_token``: the stress variant with one query centre per token)."""
     rng = _head_rng(seed, h)
     c = rng.standard_normal((centres, d), dtype=np.float32)
     t = np.arange(n)
     kc = (t // block) % centres
     k = c[kc] + np.float32(noise) * rng.standard_normal((n, d), dtype=np.float32)
-    nqb = (n + block - 1) // block
-    u = rng.integers(0, centres, size=nqb)
-    q = c[u[t // block]] + np.float32(noise) * rng.standard_normal((n, d), dtype=np.float32)
+    if per_token:
+        qc = rng.integers(0, centres, size=n)
+    else:
+        nqb = (n + block - 1) // block
+        qc = rng.integers(0, centres, size=nqb)[t // block]
+    q = c[qc] + np.float32(noise) * rng.standard_normal((n, d), dtype=np.float32)
     v = rng.standard_normal((n, d), dtype=np.float32)
     return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
 
 
-def clustered(w: Workload, heads: Optional[list] = None, threads: int = 8):
+def clustered(w: Workload, heads: Optional[list] = None, threads: int = 8,
+              per_token: bool = False):
     """bf16 bits of (Q, K, V) ``[H, N, d]`` for a named workload (all heads by default).
 
     Heads are independent streams, so they are drawn on a thread pool."""
@@ -131,7 +140,8 @@ def clustered(w: Workload, heads: Optional[list] = None, threads: int = 8):
     V = np.empty_like(Q)
 
     def one(i):
-        Q[i], K[i], V[i] = clustered_head(n, d, w.block, w.centres, w.noise, w.seed, hs[i])
+        Q[i], K[i], V[i] = clustered_head(n, d, w.block, w.centres, w.noise, w.seed, hs[i],
+                                          per_token)
 
     if threads > 1 and len(hs) > 1:
         with ThreadPoolExecutor(min(threads, len(hs))) as ex:

@@ -45,9 +45,16 @@ def tiles_rows(n, which=("first", "mid", "last"), tile=128):
     return np.array(sorted(set(rows)), dtype=np.int64)
 
 
-def sparse_with_ties(q, k, v, B, beta, rows, eps=TIE_EPS, max_ties=6):
+def sparse_with_ties(q, k, v, B, beta, rows, eps=TIE_EPS, max_ties=6, gpu_mask=None):
     """Oracle output for ``rows`` plus, for rows with near-ties, the outputs under
-    every combination of decisions on their near-tie pairs."""
+    every combination of decisions on their near-tie pairs.
+
+    A row with more than ``max_ties`` near-tie pairs is not enumerated: its
+    reference takes the GPU's own decisions on those pairs (``gpu_mask``, bool
+    ``[len(rows), nb]``, the selection the GPU computed for the same rows), the
+    reading the tie tolerance allows; the caller checks separately that the GPU
+    mask agrees with the oracle's everywhere outside the tie band.  Without a
+    GPU mask such a row is an error rather than a silently partial reference."""
     out, lse, info = O.sol_attn_head_ref(q, k, v, B, beta, rows=rows)
     ties = O.near_ties_ref(info["p"], info["mu"], info["sigma"], beta, eps)
     by_row = defaultdict(list)
@@ -55,7 +62,15 @@ def sparse_with_ties(q, k, v, B, beta, rows, eps=TIE_EPS, max_ties=6):
         by_row[i].append(j)
     cands = {}
     for i, js in by_row.items():
-        js = js[:max_ties]
+        if len(js) > max_ties:
+            assert gpu_mask is not None, (
+                f"row {int(rows[i])}: {len(js)} near-tie pairs exceed the enumeration cap "
+                f"{max_ties}; pass the GPU mask")
+            force = {(int(rows[i]), j): bool(gpu_mask[i][j]) for j in js}
+            o, l, _ = O.sol_attn_head_ref(q, k, v, B, beta, rows=[int(rows[i])], force=force,
+                                          pooled=info["pooled"])
+            cands[i] = [(o[0], l[0])]
+            continue
         opts = []
         base = info["mask"][i]
         for bits in itertools.product([False, True], repeat=len(js)):
@@ -97,6 +112,27 @@ def check_close(gpu_out, ref_out, gpu_lse=None, ref_lse=None, what="",
         le = np.abs(gpu_lse - ref_lse)
         assert le.max() <= lse_max, f"{what}: lse max|d|={le.max():.3e}"
     return err.max(), err.mean()
+
+
+# the forward computes its row statistics in moment form from this many key
+# blocks on (direct form below)
+MOMENT_MIN_BLOCKS = 128
+
+
+def route_mask(sa, q, k, v, B, beta):
+    """The GPU's selection mask ``[H, N, nb]`` (numpy bool) under the row
+    statistics the sparse forward routes with for these shapes."""
+    import torch
+    H, N, _ = q.shape
+    Nk = k.shape[1]
+    kbar, _ = sa.sol_attn_pool(k, v, B)
+    if (Nk + B - 1) // B >= MOMENT_MIN_BLOCKS:
+        mu, sigma = sa.sol_attn_row_stats_moment(q, kbar, B, Nk)
+    else:
+        mu, sigma = sa.sol_attn_row_stats(q, kbar, B, Nk)
+    m, _ = sa.sol_attn_block_mask(q, kbar, mu, sigma, beta, B, Nk)
+    torch.cuda.synchronize()
+    return m.cpu().numpy().astype(bool)
 
 
 def mask_mismatch_ok(gpu_mask, info, beta, eps=TIE_EPS):

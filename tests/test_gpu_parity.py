@@ -17,7 +17,7 @@ import block_sparse_attention_06_amd as sa  # noqa: E402
 import oracle as O  # noqa: E402
 from synth import clustered, clustered_head, gaussian, WORKLOADS  # noqa: E402
 from tests.parity_utils import (best_match, check_close, dev, host, mask_mismatch_ok,  # noqa: E402
-                                sparse_with_ties, tiles_rows)
+                                route_mask, sparse_with_ties, tiles_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -73,9 +73,11 @@ def test_proxy_and_stats_parity(case):
         kb = O.pool_ref(_head(K, h), B)
         pr = O.proxy_ref(_head(Q, h), kb)
         mr, sr = O.row_stats_ref(pr)
-        # hi/lo split of kbar: ~16 significant bits -> |dp| well below the 1e-4 tie band
-        assert np.abs(host(p[h]) - pr).max() < 5e-5
-        assert np.abs(host(mu[h]) - mr).max() < 2e-5
+        # hi/lo split of kbar: ~16 significant bits -> |dp| well below the 1e-4 tie
+        # band (measured: proxy 8.2e-6, mu 1.7e-6, sigma 9.7e-6 on the clustered
+        # tiny shape, whose scores are the largest here)
+        assert np.abs(host(p[h]) - pr).max() < 2e-5
+        assert np.abs(host(mu[h]) - mr).max() < 1e-5
         assert np.abs(host(sigma[h]) - sr).max() < 2e-5
 
 
@@ -97,10 +99,11 @@ def test_row_stats_moment_parity(H, N, B):
     for h in range(H):
         kb = O.pool_ref(_head(K, h), B)
         mr, sr = O.row_stats_ref(O.proxy_ref(_head(Q, h)[rows], kb))
-        assert np.abs(host(mu[h])[rows] - mr).max() < 2e-5
-        assert np.abs(host(sigma[h])[rows] - sr).max() < 2e-5
-    assert (mu - mu_d).abs().max().item() < 4e-5
-    assert (sigma - sigma_d).abs().max().item() < 4e-5
+        # measured at most 3.2e-7 here (1.0e-6 on clustered inputs)
+        assert np.abs(host(mu[h])[rows] - mr).max() < 5e-6
+        assert np.abs(host(sigma[h])[rows] - sr).max() < 5e-6
+    assert (mu - mu_d).abs().max().item() < 2e-5
+    assert (sigma - sigma_d).abs().max().item() < 2e-5
 
 
 @pytest.mark.parametrize("beta", [0.0, 0.5, 1.0])
@@ -189,13 +192,22 @@ def test_dense_tiny_clustered():
 
 
 def _sparse_case(Q, K, V, B, beta, heads=None, rows=None):
-    out, lse = sa.sol_attn_forward(dev(Q), dev(K), dev(V), B=B, beta=beta, mode=sa.SOL_SPARSE)
+    """Sparse forward against the oracle on the given heads and rows.  The GPU's
+    own selection (same statistics form as the forward) must match the oracle's
+    outside the tie band, and settles rows with more near-ties than the
+    enumeration covers."""
+    q, k, v = dev(Q), dev(K), dev(V)
+    out, lse = sa.sol_attn_forward(q, k, v, B=B, beta=beta, mode=sa.SOL_SPARSE)
     torch.cuda.synchronize()
     go, gl = host(out), host(lse)
+    gmask = route_mask(sa, q, k, v, B, beta)
     heads = range(Q.shape[0]) if heads is None else heads
     for h in heads:
         r = np.arange(Q.shape[1]) if rows is None else rows
-        o, l, info, cands = sparse_with_ties(_head(Q, h), _head(K, h), _head(V, h), B, beta, r)
+        o, l, info, cands = sparse_with_ties(_head(Q, h), _head(K, h), _head(V, h), B, beta, r,
+                                             gpu_mask=gmask[h][r])
+        ok, nbad = mask_mismatch_ok(gmask[h][r], info, beta)
+        assert ok, f"sparse B{B} beta{beta} h{h}: {nbad} mask mismatches outside the tie band"
         ro, rl = best_match(go[h][r], gl[h][r], o, l, cands)
         check_close(go[h][r], ro, gl[h][r], rl, what=f"sparse B{B} beta{beta} h{h}")
     return go, gl

@@ -8,6 +8,7 @@ Workloads (seeded synthetic inputs shaped like LTX-2.5 latent sequences):
   stage2 1536x1024x121f: H=32, N=24702 (24,576 video + 126 audio), B=128, seed 3
   4k     3840x2160x121f: H=32, N=130686 (130,560 + 126), B=128, 1020 centres, seed 4
   cross  audio->video  : H=32, 126 queries x 130,560 keys, N(0,1), seed 2
+and the stage-2 shape under the generator's per-token stress variant.
 """
 import numpy as np
 import pytest
@@ -25,18 +26,19 @@ pytestmark = pytest.mark.gpu
 _CACHE = {}
 
 
-def _inputs(name):
-    if name not in _CACHE:
+def _inputs(name, per_token=False):
+    key = (name, per_token)
+    if key not in _CACHE:
         _CACHE.clear()
         torch.cuda.empty_cache()
         w = WORKLOADS[name]
-        Q, K, V = clustered(w, threads=16)
-        _CACHE[name] = (w, Q, K, V, dev(Q), dev(K), dev(V))
-    return _CACHE[name]
+        Q, K, V = clustered(w, threads=16, per_token=per_token)
+        _CACHE[key] = (w, Q, K, V, dev(Q), dev(K), dev(V))
+    return _CACHE[key]
 
 
-def _check_sampled(name, beta, heads):
-    w, Q, K, V, q, k, v = _inputs(name)
+def _check_sampled(name, beta, heads, per_token=False):
+    w, Q, K, V, q, k, v = _inputs(name, per_token)
     B, N = w.block, w.n
     mode = sa.SOL_DENSE if beta == float("-inf") else sa.SOL_SPARSE
     out, lse = sa.sol_attn_forward(q, k, v, B=B, beta=beta, mode=mode)
@@ -62,8 +64,10 @@ def _check_sampled(name, beta, heads):
             o, l = O.dense_head_ref(qh, kh, vh, rows=rows)
             check_close(go[h][rows], o, gl[h][rows], l, what=f"{name} dense h{h}")
             continue
-        o, l, info, cands = sparse_with_ties(qh, kh, vh, B, beta, rows)
+        # the sampled rows are whole 128-row tiles: the tiles' masks in order
         gmask = np.concatenate([masks[int(t0)][h] for t0 in sorted(masks)])
+        assert gmask.shape[0] == len(rows)
+        o, l, info, cands = sparse_with_ties(qh, kh, vh, B, beta, rows, gpu_mask=gmask.astype(bool))
         ok, nbad = mask_mismatch_ok(gmask, info, beta)
         assert ok, f"{name} beta {beta} h{h}: {nbad} mask mismatches outside the tie band"
         ro, rl = best_match(go[h][rows], gl[h][rows], o, l, cands)
@@ -83,6 +87,12 @@ def test_stage2(beta):
 @pytest.mark.parametrize("beta", [0.5, 1.0])
 def test_4k(beta):
     _check_sampled("4k", beta, heads=(0, 31))
+
+
+def test_stage2_per_token_stress():
+    """The generator's stress variant (one query centre per token): nearly every
+    query tile needs nearly every key block."""
+    _check_sampled("stage2", 0.5, heads=(0, 31), per_token=True)
 
 
 def test_cross_attention_split_and_merge():

@@ -46,3 +46,22 @@ def test_workload_sizes():
 def test_cross_head_shapes():
     q, k, v = cross_head(126, 300, 128, seed=2, h=0)
     assert q.shape == (126, 128) and k.shape == (300, 128) and v.shape == (300, 128)
+
+
+def test_per_token_variant():
+    """The stress variant draws a centre per query token: keys and values are the
+    default recipe's, and query rows of one block no longer share a centre."""
+    base = clustered_head(1024, 128, 64, 16, 0.5, seed=0, h=0)
+    pt = clustered_head(1024, 128, 64, 16, 0.5, seed=0, h=0, per_token=True)
+    np.testing.assert_array_equal(base[1], pt[1])  # keys: drawn before the query centres
+    qb = bf16_bits_to_f32(base[0]).reshape(16, 64, 128)
+    qt = bf16_bits_to_f32(pt[0]).reshape(16, 64, 128)
+    assert 0.45 < qb.std(axis=1).mean() < 0.55        # one centre per block
+    assert qt.std(axis=1).mean() > 1.0                  # centres differ within a block
+    # the per-token centres follow the recipe's draw order
+    rng = np.random.default_rng(np.random.SeedSequence([0, 0]))
+    c = rng.standard_normal((16, 128), dtype=np.float32)
+    rng.standard_normal((1024, 128), dtype=np.float32)
+    u = rng.integers(0, 16, size=1024)
+    q = c[u] + np.float32(0.5) * rng.standard_normal((1024, 128), dtype=np.float32)
+    np.testing.assert_array_equal(pt[0], f32_to_bf16_bits(q))
