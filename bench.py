@@ -215,6 +215,37 @@ def workload_lines(sa, torch, name, to_dev, stream, reps=5, per_token=False):
     return res
 
 
+def cross_unsplit(sa, torch, qc, ks, vs, stream, halves_ms, reps=10):
+    """The audio->video cross-attention as one call over all video keys (the
+    call splits the keys over workgroups and merges the partials itself),
+    beside the two-halves-plus-merge form of the timed step.  HBM roofline:
+    K and V read once."""
+    k = torch.cat(ks, dim=1)
+    v = torch.cat(vs, dim=1)
+    H, nq, d = qc.shape
+    nk = k.shape[1]
+    out = torch.empty_like(qc)
+    lse = torch.empty((H, nq), dtype=torch.float32, device=qc.device)
+    ws = torch.empty(max(1, sa.sol_attn_workspace_size(nq, nk, H, d, 128, sa.SOL_DENSE)),
+                     dtype=torch.uint8, device=qc.device)
+    call = lambda: sa.sol_attn_forward(qc, k, v, mode=sa.SOL_DENSE, workspace=ws, out=out, lse=lse)
+    call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        call()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    kv_bytes = 2.0 * H * nk * d * 2
+    del k, v, ws
+    return {"queries": nq, "keys": nk, "ms_per_call": ms, "halves_plus_merge_ms": halves_ms,
+            "roofline": {"bound": "hbm", "achieved": kv_bytes / ms / 1e6, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": kv_bytes / ms / 1e6 / PEAK_HBM_GBS,
+                         "work": "K and V read once"}}
+
+
 def kv_sharded(sa, torch, q, k, v, B, beta, stream, dense_flops, unsplit_ms, ranks=2, reps=3):
     """Key-sharded Sol-Attn at 4K on one GPU: each rank's share of whole key
     blocks (its keys against every query, thresholds from the pooled keys of
@@ -485,6 +516,8 @@ def main():
                               "pct_bf16_peak": 100 * dense_flops / ms / 1e9 / PEAK_BF16_TFLOPS}
         extras["4k_sparse_kv_sharded"] = kv_sharded(sa, torch, q, k, v, B, args.beta, stream,
                                                     dense_flops, call_ms)
+        extras["cross_attention_unsplit"] = cross_unsplit(sa, torch, qc, (kca, kcb), (vca, vcb),
+                                                          stream, float(np.mean(cross_ms)))
         extras["fp8_projection_4k"] = fp8_projection(sa, torch, N, H * d, q.device, stream)
         log("tiny, stage-1 and stage-2 workloads")
         extras["tiny"] = workload_lines(sa, torch, "tiny", to_dev, stream, reps=20)
@@ -535,6 +568,11 @@ def main():
                           "cross_attention_halves_plus_merge": float(np.mean(cross_ms))},
         "density": {"rho_row": rho_row, "rho_tile32": rho_tile32, "rho_tile128": rho_tile128},
         "routing_hbm": hbm,
+        "cross_attention_hbm": {
+            "ms": float(np.mean(cross_ms)), "bytes": 2.0 * H * c["nk"] * d * 2,
+            "gbs": 2.0 * H * c["nk"] * d * 2 / float(np.mean(cross_ms)) / 1e6,
+            "frac": 2.0 * H * c["nk"] * d * 2 / float(np.mean(cross_ms)) / 1e6 / PEAK_HBM_GBS,
+            "work": "two split-KV halves + merge; K and V read once"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extras": extras,
