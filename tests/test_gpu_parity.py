@@ -419,3 +419,49 @@ def test_binding_rejects_mis_sized_buffers():
     out, l2 = sa.sol_attn_forward(q, q, q, B=64, beta=0.0, lse=torch.empty((H, N), device="cuda"))
     torch.cuda.synchronize()
     assert torch.isfinite(l2).all()
+
+
+# ---------------------------------------------------------------------------
+# degenerate statistics: zero spread
+# ---------------------------------------------------------------------------
+
+
+def _zero_spread(case, H=2, N=300, Nk=1000):
+    """bf16 bits of (Q, K, V) with sigma_i = 0 for every row: every key equal
+    (``same_keys``) or every query zero (``zero_queries``); 1000 keys in blocks
+    of 64 leave a ragged last block of 40."""
+    from synth import f32_to_bf16_bits
+    rng = np.random.default_rng(77)
+    q = rng.standard_normal((H, N, 128)).astype(np.float32)
+    v = rng.standard_normal((H, Nk, 128)).astype(np.float32)
+    if case == "same_keys":
+        k = np.repeat(0.2 * rng.standard_normal((H, 1, 128)).astype(np.float32), Nk, axis=1)
+    else:
+        k = rng.standard_normal((H, Nk, 128)).astype(np.float32)
+        q[:] = 0.0
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5, INF, -1e6])
+@pytest.mark.parametrize("case", ["same_keys", "zero_queries"])
+def test_zero_spread_closed_form(case, beta):
+    """sigma_i = 0: every proxy score equals mu_i, so every block ties with the
+    threshold and either decision is allowed.  Every key of a row then has the
+    same logit s_i = p_ij = mu_i, and a rejected block's Taylor weight
+    n_j e^{mu}(1 + p - mu) = n_j e^{s} equals its exact softmax mass, with the
+    block's value sum: whatever the selection, out = mean of V and
+    lse = s_i + ln(Nk).  Also one query row against one key."""
+    Q, K, V = _zero_spread(case)
+    out, lse = sa.sol_attn_forward(dev(Q), dev(K), dev(V), B=64, beta=beta, mode=sa.SOL_SPARSE)
+    torch.cuda.synchronize()
+    go, gl = host(out), host(lse)
+    for h in range(Q.shape[0]):
+        q, k, v = _head(Q, h), _head(K, h), _head(V, h)
+        s = (q @ k[0]) / math.sqrt(128)
+        check_close(go[h], np.broadcast_to(v.mean(axis=0), go[h].shape), gl[h],
+                    s + math.log(k.shape[0]), what=f"{case} beta {beta} h{h}")
+    q1, k1, v1 = (x[:1, :1].copy() for x in (Q, K, V))
+    o1, l1 = sa.sol_attn_forward(dev(q1), dev(k1), dev(v1), B=64, beta=beta, mode=sa.SOL_SPARSE)
+    torch.cuda.synchronize()
+    s1 = float(_head(q1, 0)[0] @ _head(k1, 0)[0]) / math.sqrt(128)
+    check_close(host(o1[0]), _head(v1, 0), host(l1[0]), np.array([s1]), what=f"{case} 1x1 beta {beta}")

@@ -510,3 +510,31 @@ def test_planted_mistakes_are_caught(kind):
     o, _ = f(q, k, v, 4, 1.0)
     failures += not np.allclose(o, ob, atol=1e-12)
     assert failures > 0, f"planted mistake {kind!r} passed every pin"
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.7, float("inf"), -5.0])
+def test_zero_spread_closed_form(beta):
+    """sigma_i = 0 (all keys equal, so every proxy score equals mu_i and every
+    logit equals s_i): the exact part and the Taylor part give the same mass per
+    block, so whatever the tied selection, out = mean of V and lse = s + ln(Nk).
+    Pins the oracle's sigma = 0 handling (tau = mu for finite beta, nothing
+    selected for +inf) and the Taylor weight on a ragged last block (n_j = 5)."""
+    rng = np.random.default_rng(8)
+    n, nk, d, B = 7, 37, 16, 8
+    q = rng.standard_normal((n, d))
+    k = np.repeat(rng.standard_normal((1, d)), nk, axis=0)
+    v = rng.standard_normal((nk, d))
+    out, lse, info = O.sol_attn_head_ref(q, k, v, B, beta)
+    # the spread is zero up to the rounding of the fp64 means (every score is a
+    # near-tie then, and either decision gives the same answer)
+    assert np.all(info["sigma"] < 1e-14)
+    s = q @ k[0] / math.sqrt(d)
+    np.testing.assert_allclose(out, np.broadcast_to(v.mean(axis=0), out.shape), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, s + math.log(nk), rtol=0, atol=1e-12)
+    if beta == float("inf"):
+        assert not info["mask"].any()
+    # every decision forced the other way: the same answer
+    force = {(i, j): not bool(info["mask"][i, j]) for i in range(n) for j in range(info["mask"].shape[1])}
+    fo, fl, _ = O.sol_attn_head_ref(q, k, v, B, beta, force=force)
+    np.testing.assert_allclose(fo, out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(fl, lse, rtol=0, atol=1e-12)
