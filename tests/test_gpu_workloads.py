@@ -89,6 +89,39 @@ def test_4k(beta):
     _check_sampled("4k", beta, heads=(0, 31))
 
 
+def test_4k_rows_of_every_head():
+    """4K, beta 0.5, the bench's call: four seeded random rows of every one of the
+    32 heads (whole-tile samples above cover two heads), each row against the
+    oracle, with the GPU's own selection for those rows outside the tie band."""
+    w, Q, K, V, q, k, v = _inputs("4k")
+    B, N, beta = w.block, w.n, 0.5
+    out, lse = sa.sol_attn_forward(q, k, v, B=B, beta=beta, mode=sa.SOL_SPARSE)
+    kbar, _ = sa.sol_attn_pool(k, v, B)
+    mu, sigma = sa.sol_attn_row_stats_moment(q, kbar, B, N)
+    rng = np.random.default_rng(2026)
+    picks = {h: np.sort(rng.choice(N, 4, replace=False)) for h in range(w.heads)}
+    gmasks = {}
+    for h, rows in picks.items():
+        # the inspection call takes whole 128-row tiles: each row's tile, then the row
+        sel = []
+        for r in rows:
+            t0 = int(r) // 128 * 128
+            m, _ = sa.sol_attn_block_mask(q, kbar, mu, sigma, beta, B, N, row0=t0,
+                                          nrows=min(128, N - t0))
+            sel.append(m[h, int(r) - t0].cpu().numpy())
+        gmasks[h] = np.stack(sel).astype(bool)
+    torch.cuda.synchronize()
+    for h, rows in picks.items():
+        ridx = torch.from_numpy(rows).cuda()
+        go, gl = host(out[h][ridx]), host(lse[h][ridx])
+        qh, kh, vh = (O.bf16_to_f64(x[h]) for x in (Q, K, V))
+        o, l, info, cands = sparse_with_ties(qh, kh, vh, B, beta, rows, gpu_mask=gmasks[h])
+        ok, nbad = mask_mismatch_ok(gmasks[h], info, beta)
+        assert ok, f"4k h{h}: {nbad} mask mismatches outside the tie band"
+        ro, rl = best_match(go, gl, o, l, cands)
+        check_close(go, ro, gl, rl, what=f"4k beta 0.5 h{h} rows {rows.tolist()}")
+
+
 def test_stage2_per_token_stress():
     """The generator's stress variant (one query centre per token): nearly every
     query tile needs nearly every key block."""
