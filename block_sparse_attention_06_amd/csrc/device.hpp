@@ -156,7 +156,10 @@ __device__ __forceinline__ f32x16 proxy_chunk_hl(const QFrag& qf, const u16* khi
 // M0).  Issued through inline assembly on purpose: the compiler then does not
 // treat it as a pending write to every LDS location, and does not hold the
 // following LDS reads of other buffers until it lands.  The caller orders it
-// with explicit vector-memory waits (s_waitcnt vmcnt) and barriers.
+// with explicit vector-memory waits (s_waitcnt vmcnt) and barriers.  The
+// compiler warns that M0 is reserved; the generated code of these kernels
+// never keeps a value of its own in M0 (every M0 write is one of these
+// statements, directly followed by its load: checked on the assembly by a test).
 __device__ __forceinline__ void dma_to_lds16(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :
