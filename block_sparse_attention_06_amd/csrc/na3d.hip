@@ -137,13 +137,13 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
   // Running sums relative to a reference m (log2 units) that may lag the row
-  // maximum by up to 8: o and l are rescaled only when the maximum outruns it.  Two denominators: of the bf16 probabilities the PV product
-  // uses (the output's normaliser, so the weights sum to one exactly as
-  // multiplied) and of the fp32 exponentials (for lse: with windows of a few
-  // dozen keys the bf16 rounding of p would not average out).  m starts at a
-  // finite -1e30, so that a unit without keys of this query (maximum -inf)
-  // leaves it alone and its probabilities come out 0.
-  float l = 0.f, l32 = 0.f, m = -1e30f;
+  // maximum by up to 8: o and l are rescaled only when the maximum outruns it.  The
+  // denominator l sums the fp32 exponentials before their rounding to bf16 (with
+  // windows of a few dozen keys a sum of the rounded values would carry their
+  // rounding into lse unaveraged); it normalises the output and gives lse.  m
+  // starts at a finite -1e30, so that a unit without keys of this query
+  // (maximum -inf) leaves it alone and its probabilities come out 0.
+  float l = 0.f, m = -1e30f;
   const float sl2 = 0.08838834764831845f * kLog2e;
   // column mask of element i (key column xu + acc_row(i, 0) % UC + 4g), as an
   // additive 0 / -inf bias fixed for the kernel; elements i and i + 16 / UR
@@ -155,8 +155,6 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
     const int c = xu + acc_row(i, 0) % UC + g4;
     cbias[i] = (c >= wx && c < wx + a.kx) ? 0.f : -__builtin_inff();
   }
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
 
   // unit counters (frame, nominal row-group start) of the loads and of the
   // products, advanced without divisions
@@ -215,29 +213,25 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] += cbias[i % NC];
     // Probabilities against the current reference first; the unit goes on
-    // only if the lane's bf16 row sum stays within kSlackSum (which bounds each
+    // only if the lane's row sum stays within kSlackSum (which bounds each
     // probability).  Otherwise -- a query's first unit with keys in its window
     // (the reference is still -1e30: the sums overflow), or rarely a query that
     // outran it -- the row maxima move the reference and the probabilities
     // are formed again.
     bf16x8 pb[2];
-    float rs = 0.f, rs32 = 0.f;
+    float rs = 0.f;
     auto probs = [&]() __attribute__((always_inline)) {
       float nref[UR];
 #pragma unroll
       for (int rr = 0; rr < UR; ++rr) nref[rr] = rbias[rr] - m;
       rs = 0.f;
-      rs32 = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const float e0 = fast_exp2(__builtin_fmaf(s[i], sl2, nref[acc_row(i, 0) / UC]));
         const float e1 = fast_exp2(__builtin_fmaf(s[i + 1], sl2, nref[acc_row(i + 1, 0) / UC]));
-        const __bf16 b0 = (__bf16)e0, b1 = (__bf16)e1;
-        pb[i >> 3][i & 7] = b0;
-        pb[i >> 3][(i & 7) + 1] = b1;
-        const bf16x2 pr2 = {b0, b1};
-        rs = __builtin_amdgcn_fdot2_f32_bf16(pr2, one2, rs, false);
-        rs32 += e0 + e1;
+        pb[i >> 3][i & 7] = (__bf16)e0;
+        pb[i >> 3][(i & 7) + 1] = (__bf16)e1;
+        rs += e0 + e1;
       }
     };
     probs();
@@ -255,14 +249,12 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
       const bool up = mc > m;
       const float alpha = up ? fast_exp2(m - mc) : 1.f;
       l *= alpha;
-      l32 *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
       if (up) m = mc;
       probs();
     }
     l += rs;
-    l32 += rs32;
     // O^T += V^T P^T (as in the attention kernels: two transposing reads per
     // 16-key half and 32-dim tile)
 #pragma unroll
@@ -287,7 +279,6 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
 
   // epilogue: the query's denominator is split over lanes l and l ^ 32
   const float lt = pair_sum(l);
-  const float lt32 = pair_sum(l32);
   if (!qvalid) return;
   const float inv = 1.f / lt;
   u16* orow = a.out + head + qrow * kHeadDim;
@@ -301,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void na3d_kernel(Na3dArgs a) {
       pk[1] = (uint32_t)f32_to_bf16_bits(o[dt][4 * b4 + 2] * inv) | ((uint32_t)f32_to_bf16_bits(o[dt][4 * b4 + 3] * inv) << 16);
       *reinterpret_cast<u32x2*>(orow + d0) = pk;
     }
-  if (a.lse && g == 0) a.lse[(int64_t)h * T * plane + qrow] = m * kLn2 + logf(lt32);
+  if (a.lse && g == 0) a.lse[(int64_t)h * T * plane + qrow] = m * kLn2 + logf(lt);
 }
 
 hipError_t launch_na3d(const Na3dArgs& a, hipStream_t s) {
