@@ -7,8 +7,8 @@
 // (waves 0-3) owns query rows 0-127, group 1 (waves 4-7) rows 128-255; each
 // wave owns 32 rows.  Keys stream through LDS in units of 64 rows of K and V,
 // in a ring of four stages filled by direct global->LDS loads two units ahead.
-// Per unit u each wave runs phase A -- O^T += V^T P^T for unit u-1 and
-// S^T = K Q^T for unit u, all MFMA -- and phase B -- the online softmax of
+// Per unit u each wave runs phase A -- S^T = K Q^T for unit u and
+// O^T += V^T P^T for unit u-1, all MFMA -- and phase B -- the online softmax of
 // S(u), all VALU.  The two groups run opposite phases between two barriers
 // per unit: while group 0 does A(u), group 1 does B(u-1); then group 0 does
 // B(u) while group 1 does A(u).  The two waves sharing a SIMD therefore
@@ -141,13 +141,28 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
   const char* lds_v_bytes = reinterpret_cast<const char*>(&lds_v[0][0]);
   constexpr int kStageBytes = kPPStageElems * 2;
 
-  // ---- phase A: O^T += V^T P^T for slot 0, then S^T = K Q^T for slot 1 ----
+  // ---- phase A: S^T = K Q^T for slot 1, then O^T += V^T P^T for slot 0 ----
+  // (the S products first: the softmax after the next barrier waits only for
+  // them, while the PV products' tail overlaps it; 0.5 % faster than the
+  // other order, same results)
   auto phase_a = [&](int st_prev, int st_cur) __attribute__((always_inline)) {
     if (o_rescale) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] *= o_scale;
       o_scale = 1.f;
       o_rescale = false;
+    }
+    if (qval[1] && qneed[1]) {
+      const char* kst = lds_k_bytes + st_cur * kStageBytes;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        s[kt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(kst + kaddr(ks) + kt * 32 * 256);
+          s[kt] = mfma32(as_bf16x8(ka), qf.k[ks], s[kt]);
+        }
+      }
     }
     if (qval[0] && qneed[0]) {
       const char* vst = lds_v_bytes + st_prev * kStageBytes;
@@ -168,18 +183,6 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
             }
             o[dt] = mfma32(as_bf16x8(va), pb[kt * 2 + h2], o[dt]);
           }
-        }
-      }
-    }
-    if (qval[1] && qneed[1]) {
-      const char* kst = lds_k_bytes + st_cur * kStageBytes;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        s[kt] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const u32x4 ka = *reinterpret_cast<const u32x4*>(kst + kaddr(ks) + kt * 32 * 256);
-          s[kt] = mfma32(as_bf16x8(ka), qf.k[ks], s[kt]);
         }
       }
     }
