@@ -8,7 +8,8 @@ a read of an unwritten workspace byte would show in the reference too.
 
 Cases: sparse (157 key blocks, moment-form statistics, ragged last block) then
 sparse (24 blocks, direct-form statistics); dense short-query split-KV with
-its combine, then a smaller one."""
+its combine, then a smaller one.  Last, both cases captured into one HIP graph
+and replayed with eager calls of other sizes in between."""
 import ctypes
 
 import numpy as np
@@ -94,3 +95,43 @@ def test_noalloc_rejects_oversized_call():
     r = lib.sol_attn_forward_noalloc(_p(q), _p(q), _p(q), _p(q), None, N, H, 128, 128, 0.5,
                                      sa.SOL_SPARSE, N, _stream())
     assert r == -4, r
+
+
+def test_noalloc_replays_in_a_graph():
+    """Callers that cannot allocate are typically under graph capture: the
+    entry point, set up by one eager call, captures kernels only, and every
+    replay equals the eager result bit for bit although eager calls of other
+    sizes use the same scratch between the replays."""
+    lib = sa.load_library()
+    sp = (_sparse_inputs(4, 3000, 128, 31), 128, 0.5, sa.SOL_SPARSE)
+    dn = (_dense_inputs(8, 100, 20000, 32), 128, 0.0, sa.SOL_DENSE)
+    others = [(_sparse_inputs(2, 2500, 128, 33), 128, 0.5, sa.SOL_SPARSE),
+              (_dense_inputs(16, 126, 30000, 34), 128, 0.0, sa.SOL_DENSE)]
+    eager = [_noalloc(lib, *qkv, B, beta, mode) for qkv, B, beta, mode in (sp, dn)]
+    torch.cuda.synchronize()
+
+    outs = []
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for (q, k, v), B, beta, mode in (sp, dn):
+            H, N, d = q.shape
+            out = torch.empty_like(q)
+            lse = torch.empty((H, N), dtype=torch.float32, device="cuda")
+            r = lib.sol_attn_forward_noalloc(_p(q), _p(k), _p(v), _p(out), _p(lse), N, H, d, B,
+                                             beta, mode, k.shape[1], _stream())
+            assert r == 0, sa.sol_attn_error_string(r)
+            outs.append((out, lse))
+    torch.cuda.synchronize()
+
+    for rep in range(4):
+        for o, l in outs:
+            o.fill_(float("nan"))
+            l.fill_(float("nan"))
+        # eager work between replays leaves other contents in the scratch
+        qkv, B, beta, mode = others[rep % 2]
+        _noalloc(lib, *qkv, B, beta, mode)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, ((o, l), (ro, rl)) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, ro) and torch.equal(l, rl), f"replay {rep}: call {i}"
