@@ -380,16 +380,27 @@ __global__ __launch_bounds__(256, 3) void stats_moment_kernel(StatsMomentArgs a)
   const int h = blockIdx.y;
   const u16* ch = a.chi + (int64_t)h * kHeadDim * kHeadDim;
   const u16* cl = a.clo + (int64_t)h * kHeadDim * kHeadDim;
+  // The 1280 used 16-byte chunks of each part (row tile ct keeps chunks
+  // 4 ct .. 15 of its 32 rows: 512, 384, 256, 128 chunks), five per thread,
+  // all ten loads issued before the first store.
+  u32x4 xh[5], xl[5];
+  int soff[5];
 #pragma unroll
-  for (int e = tid; e < kHeadDim * 16; e += 256) {  // all loads in flight at once
-    const int R = e >> 4, c = e & 15, ct = R >> 5;
-    if (c >= 4 * ct) {
-      const u32x4 xh = gload<u32x4>(ch + R * kHeadDim + c * 8);
-      const u32x4 xl = gload<u32x4>(cl + R * kHeadDim + c * 8);
-      const int off = (c_base(ct) + (R & 31) * c_width(ct) + c - 4 * ct) * 8;
-      *reinterpret_cast<u32x4*>(&chs[off]) = xh;
-      *reinterpret_cast<u32x4*>(&cls[off]) = xl;
-    }
+  for (int i = 0; i < 5; ++i) {
+    const int e = tid + 256 * i;
+    const int ct = (e >= 512) + (e >= 896) + (e >= 1152);
+    const int first = ct == 0 ? 0 : ct == 1 ? 512 : ct == 2 ? 896 : 1152;
+    const int w = 16 - 4 * ct, le = e - first;
+    const int rl = le / w, cu = le - rl * w;
+    const int src = (32 * ct + rl) * kHeadDim + (4 * ct + cu) * 8;
+    xh[i] = gload<u32x4>(ch + src);
+    xl[i] = gload<u32x4>(cl + src);
+    soff[i] = (c_base(ct) + rl * c_width(ct) + cu) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    *reinterpret_cast<u32x4*>(&chs[soff[i]]) = xh[i];
+    *reinterpret_cast<u32x4*>(&cls[soff[i]]) = xl[i];
   }
   if (tid < kHeadDim) mb[tid] = a.mbar[(int64_t)h * kHeadDim + tid];
   const u16* qh = a.q + (int64_t)h * a.N * kHeadDim;
