@@ -43,6 +43,16 @@ __device__ __forceinline__ T gload(const void* p) {
   return *(global_t*)p;
 }
 
+// Load of data a kernel reads once, as a stream: non-temporal, so it does not
+// displace reused lines from the caches.  Only for data whose lines one
+// instruction uses whole; a layout that touches a line from several
+// instructions would lose the line between them.
+template <typename T>
+__device__ __forceinline__ T gload_nt(const void* p) {
+  typedef const T __attribute__((address_space(1))) global_t;
+  return __builtin_nontemporal_load((global_t*)p);
+}
+
 __device__ __forceinline__ float bf16_to_f32(u16 b) { return __uint_as_float((uint32_t)b << 16); }
 
 // Round to nearest even (finite inputs).

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(Fp8QuantArgs a) {
 #pragma unroll
     for (int i = 0; i < kQuantKeep; ++i) {
       const int k = lane * 8 + i * 512;
-      keep[i] = k < a.K ? gload<u32x4>(x + k) : u32x4{0u, 0u, 0u, 0u};
+      keep[i] = k < a.K ? gload_nt<u32x4>(x + k) : u32x4{0u, 0u, 0u, 0u};  // read once
       amax = absmax8(keep[i], amax);
     }
 #pragma unroll

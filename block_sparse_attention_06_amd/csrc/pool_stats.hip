@@ -13,8 +13,9 @@ namespace solattn {
 // ---------------------------------------------------------------------------
 // Block mean-pool.  One workgroup per (key block j, head h, tensor K|V).
 // 256 threads = 16 row groups x 16 column chunks of 8 bf16 (16 B): every load
-// instruction of a wave reads 4 whole 256-byte rows (coalesced), and each
-// thread keeps all its row loads in flight before summing.
+// instruction of a wave reads 4 whole 256-byte rows (coalesced, non-temporal:
+// the keys and values are read once here), and each thread keeps all its row
+// loads in flight before summing.
 // ---------------------------------------------------------------------------
 template <int B>
 __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
@@ -28,8 +29,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     int t = rg + 16 * r;
-    x[r] = t < n ? *reinterpret_cast<const u32x4*>(src + (int64_t)t * kHeadDim + chunk * 8)
-                 : u32x4{0u, 0u, 0u, 0u};
+    x[r] = t < n ? gload_nt<u32x4>(src + (int64_t)t * kHeadDim + chunk * 8) : u32x4{0u, 0u, 0u, 0u};
   }
   float acc[8] = {};
 #pragma unroll
