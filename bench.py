@@ -30,6 +30,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA (twice the bf16 rate)
 PEAK_HBM_GBS = 8000.0
+# a sparse call without a key split orders its query tiles from this many tiles
+# in all, with at most ORDER_MAX_TILES per head (the library's launch rule)
+ORDER_MIN_TILES = 2048
+ORDER_MAX_TILES = 4096
 METRIC = "ms/call + dense-equivalent TFLOP/s (% bf16 MFMA peak), 4K Stage-2 sparse attention"
 KERNEL_SOURCES = ["block_sparse_attention_06_amd/csrc/forward.hip",
                   "block_sparse_attention_06_amd/csrc/device.hpp"]
@@ -417,26 +421,40 @@ def main():
     log(f"step {step_ms:.3f} ms  self {np.median(self_ms):.3f} ms  cross {np.median(cross_ms):.3f} ms")
 
     # routing kernels alone (same kernels as inside the call), to split the call;
-    # from 128 key blocks on the call computes the statistics in moment form
+    # from 128 key blocks on the call computes the statistics in moment form.
+    # The tile schedule call runs the call's whole prefix (pool with the
+    # forward's forms, statistics, per-tile work and order), so the fused
+    # kernel's time is the call's minus the schedule call's.
     nrep = max(3, args.steps)
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(3 * nrep)]
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4 * nrep)]
     moment = (N + B - 1) // B >= 128
+    n_qt = (N + 127) // 128
+    ordered = H * n_qt >= ORDER_MIN_TILES and n_qt <= ORDER_MAX_TILES
     mws = torch.empty(H * (2 * 128 * 128 * 2 + 128 * 4 + 8 * (128 * 128 + 2 * 128) * 4),
                       dtype=torch.uint8, device=q.device)
     for i in range(nrep):
-        e[3 * i].record(stream)
+        e[4 * i].record(stream)
         kb_, vb_ = sa.sol_attn_pool(k, v, B)
-        e[3 * i + 1].record(stream)
+        e[4 * i + 1].record(stream)
         if moment:
             mu, sigma = sa.sol_attn_row_stats_moment(q, kb_, B, N, workspace=mws)
         else:
             mu, sigma = sa.sol_attn_row_stats(q, kb_, B, N)
-        e[3 * i + 2].record(stream)
+        e[4 * i + 2].record(stream)
+        if ordered:
+            sa.sol_attn_tile_schedule(q, k, v, B=B, beta=args.beta, workspace=ws_self)
+        e[4 * i + 3].record(stream)
     torch.cuda.synchronize()
-    pool_ms = float(np.median([e[3 * i].elapsed_time(e[3 * i + 1]) for i in range(nrep)]))
-    stats_ms = float(np.median([e[3 * i + 1].elapsed_time(e[3 * i + 2]) for i in range(nrep)]))
+    med = lambda a, b: float(np.median([e[4 * i + a].elapsed_time(e[4 * i + b]) for i in range(nrep)]))
+    pool_ms, stats_ms = med(0, 1), med(1, 2)
     call_ms = float(np.mean(self_ms))
-    fwd_ms = call_ms - pool_ms - stats_ms
+    if ordered:
+        sched_ms = med(2, 3)  # pool + forms + statistics + tile work and order
+        order_ms = sched_ms - pool_ms - stats_ms
+        fwd_ms = call_ms - sched_ms
+    else:
+        order_ms = 0.0
+        fwd_ms = call_ms - pool_ms - stats_ms  # includes the forms kernel (about 13 us at 4K)
 
     # achieved density (outside the timed region)
     _, counts = sa.sol_attn_block_mask(q, kb_, mu, sigma, args.beta, B, N, want_mask=False)
@@ -564,7 +582,8 @@ def main():
         "dense_equiv_tflops_4k_sparse": call_tflops,
         "pct_bf16_peak_4k_sparse": 100 * call_tflops / PEAK_BF16_TFLOPS,
         "components_ms": {"pool": pool_ms, "row_stats": stats_ms,
-                          "fused_forward_with_forms": fwd_ms,
+                          "forms_tile_work_and_order": order_ms,
+                          "fused_forward": fwd_ms,
                           "cross_attention_halves_plus_merge": float(np.mean(cross_ms))},
         "density": {"rho_row": rho_row, "rho_tile32": rho_tile32, "rho_tile128": rho_tile128},
         "routing_hbm": hbm,

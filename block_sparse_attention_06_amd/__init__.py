@@ -35,6 +35,7 @@ __all__ = [
     "sol_attn_error_string",
     "sol_attn_proxy_scores",
     "sol_attn_block_mask",
+    "sol_attn_tile_schedule",
     "fp8_quantize_rows",
     "fp8_gemm_rowscale",
     "na3d_forward",
@@ -88,6 +89,7 @@ def load_library() -> ctypes.CDLL:
         "sol_attn_error_string": (Z, [I]),
         "sol_attn_proxy_scores": (I, [P, P, P, I, I, I, I, I, I, I, P]),
         "sol_attn_block_mask": (I, [P, P, P, P, F, I, I, I, I, I, I, I, P, P, P]),
+        "sol_attn_tile_schedule": (I, [P, P, P, P, P, I, I, I, I, F, I, P, S, P]),
         "fp8_quantize_rows": (I, [P, P, P, L, I, P]),
         "fp8_gemm_rowscale": (I, [P, P, P, P, P, I, I, I, P]),
         "na3d_forward": (I, [P, P, P, P, P, I, I, I, I, I, I, I, I, P]),
@@ -242,6 +244,36 @@ def sol_attn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, B: int =
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), N, H, d, int(B), float(beta),
         int(mode), Nk, _ptr(workspace), have, _stream(stream)))
     return out, lse
+
+
+def sol_attn_tile_schedule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, B: int = 128,
+                           beta: float = 0.5, workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Work count ``[H, ceil(N/128)]`` int32 of every 128-row query tile and the
+    order ``[H * ceil(N/128)]`` int32 (``h * n + t`` of the tile run r-th) in which
+    a sparse :func:`sol_attn_forward` call of these sizes runs them when it orders
+    its tiles."""
+    lib = load_library()
+    _want(q, "q", torch.bfloat16, 3)
+    _want(k, "k", torch.bfloat16, 3)
+    _want_shape(v, "v", torch.bfloat16, k.shape)
+    H, N, d = q.shape
+    Nk = k.shape[1]
+    if k.shape[0] != H or k.shape[2] != d:
+        raise ValueError("k and v must be [H, Nk, d] with q's H and d")
+    if math.isnan(beta):
+        raise ValueError("beta must not be NaN")
+    n_qt = (N + 127) // 128
+    work = torch.empty((H, n_qt), dtype=torch.int32, device=q.device)
+    order = torch.empty((H * n_qt,), dtype=torch.int32, device=q.device)
+    ws_bytes = sol_attn_workspace_size(N, Nk, H, d, B, SOL_SPARSE)
+    if workspace is None:
+        workspace = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=q.device)
+    have = _want_ws(workspace)
+    _check("sol_attn_tile_schedule", lib.sol_attn_tile_schedule(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(work), _ptr(order), N, H, d, int(B), float(beta), Nk,
+        _ptr(workspace), have, _stream(stream)))
+    return work, order
 
 
 def sol_attn_forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

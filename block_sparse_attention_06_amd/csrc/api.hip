@@ -29,6 +29,10 @@ constexpr int kSplitTarget = 2 * kCUs;
 // From this many key blocks on, the row statistics use the moment form (2 d^2
 // multiply-adds per row instead of 2 d nb).
 constexpr int kMomentMinBlocks = 128;
+// From this many query tiles on (four rounds of two workgroups per CU), a
+// sparse call without a key split runs each head's tiles in order of
+// decreasing work (tile_work_kernel, tile_order_kernel).
+constexpr long long kOrderMinTiles = 4LL * 2 * kCUs;
 constexpr size_t kMomentBytesPerHead = 2 * 128 * 128 * sizeof(uint16_t) + 128 * sizeof(float) +
                                        (size_t)kMomentSplits * kMomentPartFloats * sizeof(float);
 
@@ -66,7 +70,8 @@ struct Plan {
   int max_splits;
   size_t off_kbar, off_vbar, off_vsum, off_khi, off_klo, off_mu, off_sigma, off_po, off_pml, bytes;
   size_t off_chi, off_clo, off_mbar, off_mpart;  // moment-form statistics (nb >= kMomentMinBlocks)
-  bool moments;
+  size_t off_work, off_order;                     // tile order (sparse, no key split, many tiles)
+  bool moments, order;
 };
 
 // Sizes are validated by the caller.  A sparse-mode workspace also covers the
@@ -101,6 +106,12 @@ Plan make_plan(int N, int Nk, int H, int B, int mode) {
       p.off_clo = take((size_t)H * 128 * 128 * sizeof(uint16_t));
       p.off_mbar = take((size_t)H * 128 * sizeof(float));
     p.off_mpart = take((size_t)H * kMomentSplits * kMomentPartFloats * sizeof(float));
+    }
+    const int n_qt = cdiv(N, 128);
+    p.order = p.sp.splits == 1 && (long long)H * n_qt >= kOrderMinTiles && n_qt <= kOrderMaxTiles;
+    if (p.order) {
+      p.off_work = take((size_t)H * n_qt * sizeof(int));
+      p.off_order = take((size_t)H * n_qt * sizeof(int));
     }
   }
   if (p.max_splits > 1) {
@@ -178,6 +189,38 @@ int check_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   return SOL_OK;
 }
 
+// The routing steps of a sparse call on a checked, large enough workspace:
+// block means of keys and values with the forward kernel's forms, then the
+// row statistics (moment form from kMomentMinBlocks blocks on).
+struct Routing {
+  PoolArgs pool;
+  float* mu;
+  float* sigma;
+};
+
+int route(const uint16_t* q, const uint16_t* k, const uint16_t* v, int N, int H, int B, int Nk,
+          const Plan& p, char* ws, hipStream_t s, Routing* out) {
+  const Split& sp = p.sp;
+  PoolArgs pa{k, v, (float*)(ws + p.off_kbar), (float*)(ws + p.off_vbar),
+              (uint16_t*)(ws + p.off_vsum), (uint16_t*)(ws + p.off_khi),
+              (uint16_t*)(ws + p.off_klo), Nk, H, B, sp.nb, sp.nb_pad};
+  if (int r = hip_status(launch_pool(pa, s))) return r;
+  float* mu = (float*)(ws + p.off_mu);
+  float* sigma = (float*)(ws + p.off_sigma);
+  if (p.moments) {
+    MomentArgs ma{pa.kbar, (uint16_t*)(ws + p.off_chi), (uint16_t*)(ws + p.off_clo),
+                  (float*)(ws + p.off_mbar), (float*)(ws + p.off_mpart), H, sp.nb};
+    if (int r = hip_status(launch_moments(ma, s))) return r;
+    StatsMomentArgs sm{q, ma.chi, ma.clo, ma.mbar, mu, sigma, N, H};
+    if (int r = hip_status(launch_stats_moment(sm, s))) return r;
+  } else {
+    StatsArgs sa{q, pa.kbar, mu, sigma, N, H, sp.nb};
+    if (int r = hip_status(launch_stats(sa, s))) return r;
+  }
+  *out = Routing{pa, mu, sigma};
+  return SOL_OK;
+}
+
 // Launches of the forward call on a checked, large enough workspace.
 int forward_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
                    float* lse, int N, int H, int B, float beta, int mode, int Nk, const Plan& p,
@@ -195,23 +238,16 @@ int forward_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint
   f.splits = sp.splits; f.tiles_per_split = sp.tiles_per_split;
   f.total = H * f.n_qt * f.splits;
   if (sparse) {
-    PoolArgs pa{k, v, (float*)(ws + p.off_kbar), (float*)(ws + p.off_vbar),
-                (uint16_t*)(ws + p.off_vsum), (uint16_t*)(ws + p.off_khi),
-                (uint16_t*)(ws + p.off_klo), Nk, H, B, sp.nb, sp.nb_pad};
-    if (int r = hip_status(launch_pool(pa, s))) return r;
-    float* mu = (float*)(ws + p.off_mu);
-    float* sigma = (float*)(ws + p.off_sigma);
-    if (p.moments) {
-      MomentArgs ma{pa.kbar, (uint16_t*)(ws + p.off_chi), (uint16_t*)(ws + p.off_clo),
-                    (float*)(ws + p.off_mbar), (float*)(ws + p.off_mpart), H, sp.nb};
-      if (int r = hip_status(launch_moments(ma, s))) return r;
-      StatsMomentArgs sm{q, ma.chi, ma.clo, ma.mbar, mu, sigma, N, H};
-      if (int r = hip_status(launch_stats_moment(sm, s))) return r;
-    } else {
-      StatsArgs sa{q, pa.kbar, mu, sigma, N, H, sp.nb};
-      if (int r = hip_status(launch_stats(sa, s))) return r;
+    Routing rt;
+    if (int r = route(q, k, v, N, H, B, Nk, p, ws, s, &rt)) return r;
+    f.khi = rt.pool.khi; f.klo = rt.pool.klo; f.vsumT = rt.pool.vsumT;
+    f.mu = rt.mu; f.sigma = rt.sigma;
+    if (p.order) {
+      TileOrderArgs ta{q, rt.pool.khi, rt.pool.klo, rt.mu, rt.sigma, (int*)(ws + p.off_work),
+                       (int*)(ws + p.off_order), beta, N, H, sp.nb, sp.nb_pad, f.n_qt};
+      if (int r = hip_status(launch_tile_order(ta, s))) return r;
+      f.order = ta.order;
     }
-    f.khi = pa.khi; f.klo = pa.klo; f.vsumT = pa.vsumT; f.mu = mu; f.sigma = sigma;
   }
   if (f.splits > 1) {
     f.part_o = (float*)(ws + p.off_po);
@@ -387,6 +423,24 @@ int sol_attn_forward_noalloc(const uint16_t* q, const uint16_t* k, const uint16_
     if (int r = scratch_of_stream_device(stream, &ws)) return r;
   }
   return forward_launch(q, k, v, out, lse, N, H, B, beta, mode, Nk, p, ws, stream);
+}
+
+int sol_attn_tile_schedule(const uint16_t* q, const uint16_t* k, const uint16_t* v, int* work,
+                           int* order, int N, int H, int d, int B, float beta, int Nk,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  if (Nk == 0) Nk = N;
+  if (!work || !order) return SOL_ERR_INVALID_ARG;
+  if (isinf(beta) && beta < 0) return SOL_ERR_INVALID_ARG;  // dense: no selection to count
+  if (int r = check_forward(q, k, v, q, N, H, d, B, beta, SOL_SPARSE, Nk)) return r;
+  if (cdiv(N, 128) > kOrderMaxTiles) return SOL_ERR_UNSUPPORTED;
+  const Plan p = make_plan(N, Nk, H, B, SOL_SPARSE);
+  if (!workspace || ws_bytes < p.bytes || !aligned(workspace, 256)) return SOL_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  Routing rt;
+  if (int r = route(q, k, v, N, H, B, Nk, p, (char*)workspace, s, &rt)) return r;
+  TileOrderArgs ta{q, rt.pool.khi, rt.pool.klo, rt.mu, rt.sigma, work, order, beta, N, H,
+                   p.sp.nb, p.sp.nb_pad, cdiv(N, 128)};
+  return hip_status(launch_tile_order(ta, s));
 }
 
 size_t sol_attn_shard_workspace_size(int N, int Nk, int nb_all, int H, int d, int B,

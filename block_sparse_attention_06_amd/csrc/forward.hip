@@ -62,13 +62,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int g4 = g * 4;  // accumulator element i of lane half g is row acc_row(i, 0) + g4
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // Natural order: consecutive workgroups take consecutive query tiles of one
-  // head and are dealt to the 8 XCDs round-robin, so all XCDs work on the same
-  // one or two heads at a time.
+  // Consecutive workgroups take query tiles of one head and are dealt to the
+  // 8 XCDs round-robin, so all XCDs work on the same one or two heads at a
+  // time; within a head either in natural order or, for a sparse call without
+  // a key split, in the order of decreasing work (a.order).
   const int logical = blockIdx.x;
   if (logical >= a.total) return;
   const int split = logical % a.splits;
-  const int tq = logical / a.splits;
+  const int tq = a.order ? a.order[logical] : logical / a.splits;
   const int qt = tq % a.n_qt, h = tq / a.n_qt;
   const int row = qt * kQTile + wave * 32 + r32;
   const bool qvalid = row < a.N;

@@ -122,6 +122,21 @@ struct FwdArgs {
   int n_qt;            // query tiles (32 rows per wave)
   int splits, tiles_per_split;
   int total;           // H * n_qt * splits
+  const int* order;    // splits == 1: [H * n_qt] query tile of each workgroup, or null
+};
+
+// Order of the query tiles of a sparse call: each tile's work (key blocks any
+// of its rows selects) counted, then each head's tiles ranked by it.
+struct TileOrderArgs {
+  const uint16_t* q;
+  const uint16_t* khi;  // routing forms of the pooled keys, as FwdArgs
+  const uint16_t* klo;
+  const float* mu;
+  const float* sigma;
+  int* work;            // [H, n_qt] (written)
+  int* order;           // [H * n_qt] (written)
+  float beta;
+  int N, H, nb, nb_pad, n_qt;
 };
 
 struct CombineArgs {
@@ -158,6 +173,8 @@ hipError_t launch_moments(const MomentArgs& a, hipStream_t s);
 hipError_t launch_stats_moment(const StatsMomentArgs& a, hipStream_t s);
 hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t s);
+hipError_t launch_tile_order(const TileOrderArgs& a, hipStream_t s);
+constexpr int kOrderMaxTiles = 4096;  // query tiles per head the rank kernel holds in LDS
 hipError_t launch_forward(const FwdArgs& a, bool sparse, int B, hipStream_t s);
 hipError_t launch_forward_pp(const FwdArgs& a, hipStream_t s);  // dense only
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

@@ -463,6 +463,129 @@ hipError_t launch_stats_moment(const StatsMomentArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Order of the query tiles of a sparse call.
+//
+// The fused kernel loads, for each 128-row tile, every key block one of its
+// rows selects, and the two workgroups of each CU stream those blocks through
+// the L2 of their XCD.  Workgroups that run at the same time on one XCD share
+// those lines only while their key sweeps stay close, which holds when their
+// tiles carry about the same work.  So each tile's work -- the number of
+// blocks any of its rows selects, by the forward kernel's predicate on proxy
+// scores from the high part of the pooled keys -- is counted first, and each
+// head's tiles are then launched in order of decreasing work (ties by tile
+// index).  The order changes only when a tile runs, never what it computes.
+//
+// tile_work_kernel: one workgroup per (two 128-row tiles, head), 8 waves of
+// 32 rows (waves 0-3 the first tile, 4-7 the second).  The proxy scores use
+// the bf16 high part of the pooled keys only: the count ranks tiles, and a
+// decision can differ from the forward kernel's only where a proxy lies
+// within about 2^-9 of the row's threshold scale.  Each chunk of 32 pooled
+// keys (8 KiB) is staged once per workgroup by direct global->LDS loads, one
+// instruction per wave, in a ring of three stages filled two chunks ahead;
+// chunk c of block row r sits at slot c ^ (r % 16), so the operand reads of
+// 16 consecutive rows at one chunk are conflict-free.  One barrier per chunk:
+// it publishes the chunk's loads and the previous chunk's wave masks, whose
+// union a lane of waves 0 and 4 then counts.
+constexpr int kWorkStages = 3;
+constexpr int kWorkStageBytes = kChunk * kHeadDim * 2;  // 8 KiB
+constexpr int kWorkWaitOne = 0x0F71;                    // s_waitcnt vmcnt(1)
+
+__global__ __launch_bounds__(512) void tile_work_kernel(TileOrderArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 stage[kWorkStages][kWorkStageBytes / 2];
+  __shared__ uint32_t wmask[2][8];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, r = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.y;
+  const int qt = blockIdx.x * 2 + (wave >> 2);  // this wave's tile
+  const int row = qt * kQTile + (wave & 3) * 32 + r;
+  const bool valid = row < a.N;
+  QFrag qf;
+  load_qfrag(qf, a.q + (int64_t)h * a.N * kHeadDim, row, valid, g);
+  float tau = __builtin_inff();
+  if (valid) tau = make_tau(a.mu[(int64_t)h * a.N + row], a.sigma[(int64_t)h * a.N + row], a.beta);
+  // the only loads the compiler tracks: drained here, so none of its waits
+  // depends on the direct loads below
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // direct loads: wave w fills 16-byte slots 64 w .. 64 w + 63 of a stage,
+  // slot P holding chunk (P % 16) ^ (row % 16) of block row P / 16
+  const int P = wave * 64 + lane, srow = P >> 4, sc = (P & 15) ^ (srow & 15);
+  const u16* src = a.khi + ((int64_t)h * a.nb_pad + srow) * kHeadDim + sc * 8;
+  const int n_chunks = a.nb_pad / kChunk;
+  auto dma_chunk = [&](int c, int st) __attribute__((always_inline)) {
+    c = c < n_chunks ? c : n_chunks - 1;  // past the end: a stage never read again
+    dma_to_lds16(src + (int64_t)c * kChunk * kHeadDim, lds_addr(&stage[st][wave * 64 * 8]));
+  };
+  dma_chunk(0, 0);
+  dma_chunk(1, 1);
+  int work = 0;
+  const bool counter = lane == 0 && (wave & 3) == 0;  // lane 0 of waves 0 and 4
+  const int tbase = wave & 4;
+  for (int c = 0; c < n_chunks; ++c) {
+    __builtin_amdgcn_s_waitcnt(kWorkWaitOne);  // this wave's load of chunk c landed
+    __builtin_amdgcn_s_barrier();              // every wave's; stage of c - 1 read
+    asm volatile("" ::: "memory");
+    dma_chunk(c + 2, (c + 2) % kWorkStages);
+    if (counter && c > 0) {
+      const uint32_t* m = wmask[(c - 1) & 1] + tbase;
+      work += __popc(m[0] | m[1] | m[2] | m[3]);
+    }
+    const u16* st = stage[c % kWorkStages];
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(st + (r * 16 + ((2 * ks + g) ^ (r & 15))) * 8);
+      acc = mfma32(hi, qf.k[ks], acc);
+    }
+    const float scale = 0.08838834764831845f;  // 1/sqrt(128)
+    const int b0 = c * kChunk;
+    uint32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int off = acc_row(i, g);
+      mine |= (uint32_t)(valid && b0 + off < a.nb && is_selected(acc[i] * scale, tau)) << off;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mine |= __shfl_xor(mine, o);
+    if (lane == 0) wmask[c & 1][wave] = mine;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if (counter && qt < a.n_qt) {
+    const uint32_t* m = wmask[(n_chunks - 1) & 1] + tbase;
+    work += __popc(m[0] | m[1] | m[2] | m[3]);
+    a.work[(int64_t)h * a.n_qt + qt] = work;
+  }
+}
+
+// tile_order_kernel: one workgroup per head.  Tile i's rank is the number of
+// tiles with more work, or as much work and a smaller index; the tile of rank
+// r runs as the head's r-th workgroup.
+__global__ __launch_bounds__(1024) void tile_order_kernel(TileOrderArgs a) {
+  __shared__ int work[kOrderMaxTiles];
+  const int h = blockIdx.x, n = a.n_qt;
+  for (int i = threadIdx.x; i < n; i += 1024) work[i] = a.work[(int64_t)h * n + i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += 1024) {
+    const int w = work[i];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+      const int wj = work[j];
+      rank += (wj > w) | ((wj == w) & (j < i));
+    }
+    a.order[(int64_t)h * n + rank] = h * n + i;
+  }
+}
+
+hipError_t launch_tile_order(const TileOrderArgs& a, hipStream_t s) {
+  if (a.n_qt > kOrderMaxTiles) return hipErrorInvalidValue;
+  const hipError_t e = launch_kernel(tile_work_kernel, dim3((a.n_qt + 1) / 2, a.H), dim3(512), s, a);
+  if (e != hipSuccess) return e;
+  return launch_kernel(tile_order_kernel, dim3(a.H), dim3(1024), s, a);
+}
+
+// ---------------------------------------------------------------------------
 // Inspection: proxy scores of a row range.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void proxy_kernel(ProxyArgs a) {

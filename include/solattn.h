@@ -172,6 +172,36 @@ int sol_attn_forward_noalloc(const uint16_t* q, const uint16_t* k, const uint16_
                              int mode, int Nk, void* stream);
 
 /*
+ * Inspection: the order in which sol_attn_forward (SOL_SPARSE) runs the
+ * 128-row query tiles of each head.
+ *   Sol-Engine LTX25 page, "Stage 2 Optimization -- Core Technology: Sol-Attn",
+ *   bullet "Query-dependent thresholding": every row selects its own key
+ *   blocks, so the 128-row tiles of a head carry different amounts of work
+ *   (the blocks any of their rows selects).
+ * The forward call, for a sparse call without a key split and with at least
+ * 2048 tiles in all (4 x 2 x 256 CUs) and at most 4096 tiles per head, counts
+ * each tile's work and launches each head's tiles in order of decreasing work
+ * (ties by tile index); the order decides only when a tile runs, never its
+ * result.  This entry point runs the same steps (pool, row statistics, work
+ * count, ranking) for any such call size and returns their results:
+ * work     [H, ceil(N/128)] int32 (written): per tile, the key blocks one of
+ *          its rows selects -- by the forward predicate on proxy scores from
+ *          the bf16 high part of the pooled keys, so a pair within about
+ *          2^-9 of its row's threshold scale may count differently from the
+ *          forward kernel's decision.
+ * order    [H * ceil(N/128)] int32 (written): order[h * n + r] = h * n + t
+ *          for the tile t of head h that runs r-th (n = ceil(N/128)).
+ * q, k, v, N, H, d, B, beta, Nk as sol_attn_forward (SOL_SPARSE); beta = -inf
+ * is SOL_ERR_INVALID_ARG (nothing to count), more than 4096 tiles per head
+ * SOL_ERR_UNSUPPORTED.
+ * workspace, ws_bytes: at least sol_attn_workspace_size(N, Nk, H, d, B,
+ *          SOL_SPARSE) bytes, 256-byte aligned.
+ */
+int sol_attn_tile_schedule(const uint16_t* q, const uint16_t* k, const uint16_t* v, int* work,
+                           int* order, int N, int H, int d, int B, float beta, int Nk,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Exact merge of two partial answers over disjoint key sets.
  *   doubleAI page, "Attention across two GPUs": each partial carries its
  *   running maximum and sum of exponentials (here as lse) and merges exactly.

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
               "sol_attn_row_stats_moment", "sol_attn_workspace_size", "sol_attn_error_string", "sol_attn_proxy_scores",
               "sol_attn_block_mask", "fp8_quantize_rows", "fp8_gemm_rowscale", "na3d_forward",
               "sol_attn_forward_shard", "sol_attn_shard_workspace_size",
-              "sol_attn_combine_partials"):
+              "sol_attn_combine_partials", "sol_attn_tile_schedule"):
         assert n in names
 
 
@@ -104,6 +104,14 @@ def test_other_entry_points_argument_errors(lib):
                                    N, FAKE, N) == -1          # row0 not a multiple of 128
     assert lib.sol_attn_block_mask(FAKE, FAKE, FAKE, FAKE, math.nan, 0, 10, 256, 256, 1, 128,
                                    64, N, FAKE, N) == -1
+    ts = lib.sol_attn_tile_schedule
+    big = 1 << 40
+    assert ts(FAKE, FAKE, FAKE, N, FAKE, 256, 1, 128, 128, 0.5, 0, FAKE, big, N) == -1  # no work
+    assert ts(FAKE, FAKE, FAKE, FAKE, FAKE, 256, 1, 128, 128, -math.inf, 0, FAKE, big, N) == -1
+    assert ts(FAKE, FAKE, FAKE, FAKE, FAKE, 256, 1, 128, 128, math.nan, 0, FAKE, big, N) == -1
+    assert ts(FAKE, FAKE, FAKE, FAKE, FAKE, 256, 1, 128, 96, 0.5, 0, FAKE, big, N) == -2   # B
+    assert ts(FAKE, FAKE, FAKE, FAKE, FAKE, 256, 1, 128, 128, 0.5, 0, FAKE, 16, N) == -1   # short ws
+    assert ts(FAKE, FAKE, FAKE, FAKE, FAKE, 4097 * 128, 1, 128, 128, 0.5, 0, FAKE, big, N) == -2
 
 
 def test_shard_entry_points_argument_errors(lib):
