@@ -40,6 +40,14 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Whether a launch without a key split runs its query tiles in order of
+// decreasing work (enough tiles for several rounds of workgroups, and few
+// enough per head for the rank kernel's LDS).
+bool orders_tiles(int N, int H) {
+  const int n_qt = cdiv(N, 128);
+  return (long long)H * n_qt >= kOrderMinTiles && n_qt <= kOrderMaxTiles;
+}
+
 struct Split {
   int nb, nb_pad, splits, tiles_per_split;
 };
@@ -107,11 +115,10 @@ Plan make_plan(int N, int Nk, int H, int B, int mode) {
       p.off_mbar = take((size_t)H * 128 * sizeof(float));
     p.off_mpart = take((size_t)H * kMomentSplits * kMomentPartFloats * sizeof(float));
     }
-    const int n_qt = cdiv(N, 128);
-    p.order = p.sp.splits == 1 && (long long)H * n_qt >= kOrderMinTiles && n_qt <= kOrderMaxTiles;
+    p.order = p.sp.splits == 1 && orders_tiles(N, H);
     if (p.order) {
-      p.off_work = take((size_t)H * n_qt * sizeof(int));
-      p.off_order = take((size_t)H * n_qt * sizeof(int));
+      p.off_work = take((size_t)H * cdiv(N, 128) * sizeof(int));
+      p.off_order = take((size_t)H * cdiv(N, 128) * sizeof(int));
     }
   }
   if (p.max_splits > 1) {
@@ -129,9 +136,10 @@ Plan make_plan(int N, int Nk, int H, int B, int mode) {
 struct ShardPlan {
   int nb, nb_pad;
   size_t off_kbar, off_vbar, off_vsum, off_khi, off_klo, off_mu, off_sigma;
-  size_t off_chi, off_clo, off_mbar, off_mpart, bytes;
-  bool moments;
+  size_t off_chi, off_clo, off_mbar, off_mpart, off_work, off_order, bytes;
+  bool moments, order;
 };
+
 
 ShardPlan make_shard_plan(int N, int Nk, int nb_all, int H, int B, bool sparse) {
   ShardPlan p{};
@@ -158,6 +166,12 @@ ShardPlan make_shard_plan(int N, int Nk, int nb_all, int H, int B, bool sparse) 
     p.off_clo = take((size_t)H * 128 * 128 * sizeof(uint16_t));
     p.off_mbar = take((size_t)H * 128 * sizeof(float));
     p.off_mpart = take((size_t)H * kMomentSplits * kMomentPartFloats * sizeof(float));
+  }
+  // the share's tiles in order of decreasing work over its own blocks
+  p.order = orders_tiles(N, H);
+  if (p.order) {
+    p.off_work = take((size_t)H * cdiv(N, 128) * sizeof(int));
+    p.off_order = take((size_t)H * cdiv(N, 128) * sizeof(int));
   }
   p.bytes = off;
   return p;
@@ -500,6 +514,12 @@ int sol_attn_forward_shard(const uint16_t* q, const uint16_t* k, const uint16_t*
       if (int r = hip_status(launch_stats(sa, s))) return r;
     }
     f.khi = pa.khi; f.klo = pa.klo; f.vsumT = pa.vsumT; f.mu = mu; f.sigma = sigma;
+    if (p.order) {
+      TileOrderArgs ta{q, pa.khi, pa.klo, mu, sigma, (int*)(ws + p.off_work),
+                       (int*)(ws + p.off_order), beta, N, H, p.nb, p.nb_pad, f.n_qt};
+      if (int r = hip_status(launch_tile_order(ta, s))) return r;
+      f.order = ta.order;
+    }
   }
   return hip_status(launch_forward(f, sparse, sparse ? B : 128, s));
 }
