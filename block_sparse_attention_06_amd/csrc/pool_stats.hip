@@ -539,14 +539,18 @@ __global__ __launch_bounds__(512) void tile_work_kernel(TileOrderArgs a) {
     }
     const float scale = 0.08838834764831845f;  // 1/sqrt(128)
     const int b0 = c * kChunk;
+    // the wave's union per block from one ballot per accumulator element: lanes
+    // 0-31 hold block acc_row(i, 0) of their rows, lanes 32-63 block acc_row(i, 1)
+    // (invalid rows have tau = +inf and select nothing)
     uint32_t mine = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int off = acc_row(i, g);
-      mine |= (uint32_t)(valid && b0 + off < a.nb && is_selected(acc[i] * scale, tau)) << off;
+      const uint64_t b = __builtin_amdgcn_ballot_w64(is_selected(acc[i] * scale, tau));
+      mine |= ((uint32_t)b != 0u ? 1u : 0u) << acc_row(i, 0);
+      mine |= ((uint32_t)(b >> 32) != 0u ? 1u : 0u) << acc_row(i, 1);
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) mine |= __shfl_xor(mine, o);
+    const int left = a.nb - b0;  // blocks of this chunk that exist
+    if (left < 32) mine &= (1u << left) - 1u;
     if (lane == 0) wmask[c & 1][wave] = mine;
   }
   __builtin_amdgcn_s_waitcnt(0);
