@@ -1,5 +1,6 @@
 """The library's calls under HIP graph capture: every entry point used on the
-hot path enqueues kernels only (no allocation, no memset, no synchronisation),
+hot path enqueues kernels only (no allocation, no memset, no synchronisation;
+the sparse calls include one large enough to order its query tiles),
 so a captured sequence replays to the eager results bit for bit.  The graph
 is replayed several times with eager work and synchronisations in between,
 and every replay is checked (the kernels are deterministic)."""
@@ -34,6 +35,11 @@ def test_hot_path_replays_in_a_graph():
     ka, kb_ = k[:, :half].contiguous(), k[:, half:].contiguous()
     va, vb = v[:, :half].contiguous(), v[:, half:].contiguous()
     kbar_all, _ = sa.sol_attn_pool(k, v, B)
+    # 16 heads x 128 query tiles: the call runs its tiles in order of decreasing work
+    Qo, Ko, Vo = _clustered(16, 16384, B, 128, seed=23)
+    qo, ko, vo = dev(Qo), dev(Ko), dev(Vo)
+    ws_o = torch.empty(sa.sol_attn_workspace_size(16384, 16384, 16, 128, B, sa.SOL_SPARSE),
+                       dtype=torch.uint8, device="cuda")
     grid = (4, 12, 20)
     Qn, Kn, Vn = gaussian(2, int(np.prod(grid)), 128, seed=22)
     qn, kn, vn = dev(Qn), dev(Kn), dev(Vn)
@@ -42,6 +48,7 @@ def test_hot_path_replays_in_a_graph():
         f32, bf = torch.float32, torch.bfloat16
         return dict(
             o_sp=torch.empty_like(q), l_sp=torch.empty((H, N), dtype=f32, device="cuda"),
+            o_or=torch.empty_like(qo), l_or=torch.empty((16, 16384), dtype=f32, device="cuda"),
             o_dn=torch.empty_like(q), l_dn=torch.empty((H, N), dtype=f32, device="cuda"),
             o_a=torch.empty_like(qs), l_a=torch.empty((H, 126), dtype=f32, device="cuda"),
             o_b=torch.empty_like(qs), l_b=torch.empty((H, 126), dtype=f32, device="cuda"),
@@ -67,6 +74,8 @@ def test_hot_path_replays_in_a_graph():
 
     def run(b):
         sa.sol_attn_forward(q, k, v, B=B, beta=0.5, workspace=ws, out=b["o_sp"], lse=b["l_sp"])
+        sa.sol_attn_forward(qo, ko, vo, B=B, beta=0.5, workspace=ws_o, out=b["o_or"],
+                            lse=b["l_or"])
         sa.sol_attn_forward(q, k, v, mode=sa.SOL_DENSE, workspace=ws, out=b["o_dn"],
                             lse=b["l_dn"])
         sa.sol_attn_forward(qs, ka, va, mode=sa.SOL_DENSE, workspace=ws_a, out=b["o_a"],

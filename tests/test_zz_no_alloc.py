@@ -7,8 +7,9 @@ reference calls is filled with 0xFF bytes (NaN in every float format) so that
 a read of an unwritten workspace byte would show in the reference too.
 
 Cases: sparse (157 key blocks, moment-form statistics, ragged last block) then
-sparse (24 blocks, direct-form statistics); dense short-query split-KV with
-its combine, then a smaller one.  Last, both cases captured into one HIP graph
+sparse (24 blocks, direct-form statistics); sparse with 2,048 query tiles, which
+the call runs in order of decreasing work, then a small one; dense short-query
+split-KV with its combine, then a smaller one.  Last, both cases captured into one HIP graph
 and replayed with eager calls of other sizes in between."""
 import ctypes
 
@@ -67,12 +68,15 @@ def _dense_inputs(H, nq, nk, seed):
     return dev(Q), dev(K), dev(V)
 
 
-@pytest.mark.parametrize("case", ["sparse", "dense_split"])
+@pytest.mark.parametrize("case", ["sparse", "sparse_ordered", "dense_split"])
 def test_noalloc_matches_workspace_call_twice(case):
     lib = sa.load_library()
     if case == "sparse":
         calls = [(_sparse_inputs(8, 20000, 128, 21), 128, 0.5, sa.SOL_SPARSE),
                  (_sparse_inputs(2, 3000, 128, 22), 128, 0.5, sa.SOL_SPARSE)]
+    elif case == "sparse_ordered":  # 16 x 128 tiles: the call orders them (tile work and order in scratch)
+        calls = [(_sparse_inputs(16, 16384, 128, 25), 128, 0.5, sa.SOL_SPARSE),
+                 (_sparse_inputs(2, 3000, 128, 26), 128, 1.0, sa.SOL_SPARSE)]
     else:
         calls = [(_dense_inputs(16, 126, 40000, 23), 128, 0.0, sa.SOL_DENSE),
                  (_dense_inputs(4, 100, 9000, 24), 128, 0.0, sa.SOL_DENSE)]
