@@ -205,7 +205,7 @@ __global__ __launch_bounds__(512, 2) void fwd_pp_kernel(FwdArgs a) {
       for (int i = 0; i < 16; ++i) {
         const float e = fast_exp2(__builtin_fmaf(s[kt][i], sl2, neg_ref));
         pb[kt * 2 + (i >> 3)][i & 7] = (__bf16)e;
-        rsum[i & 3] += e;
+        rsum[i & 3] = (kt == 0 && i < 4) ? e : rsum[i & 3] + e;  // first term: no +0
       }
     return (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
   };
