@@ -61,9 +61,10 @@ def test_schedule_counts_and_order(H, N, B, beta):
         np.testing.assert_array_equal(o[h * n_qt:(h + 1) * n_qt], want, err_msg=f"head {h}")
 
 
-def test_ordered_call_equals_natural_order_calls():
-    H, N, B, beta = 4, 65536, 128, 0.5  # 4 x 512 tiles: the call orders; one head: 512 tiles, no split
-    q, k, v = _inputs(H, N, seed=47)
+@pytest.mark.parametrize("B,beta", [(128, 0.5), (64, 1.0)])
+def test_ordered_call_equals_natural_order_calls(B, beta):
+    H, N = 4, 65536  # 4 x 512 tiles: the call orders; one head: 512 tiles, no split
+    q, k, v = _inputs(H, N, seed=47, B=B)
     out = torch.full_like(q, float("nan"))
     lse = torch.full((H, N), float("nan"), dtype=torch.float32, device="cuda")
     sa.sol_attn_forward(q, k, v, B=B, beta=beta, out=out, lse=lse)
