@@ -1,5 +1,7 @@
-// Routing kernels: block mean-pool, proxy-score row statistics, and the two
-// inspection kernels (proxy scores of a row range, block selection mask).
+// Routing kernels: block mean-pool, proxy-score row statistics, the launch
+// order of a sparse call's query tiles (per-tile work count and per-head
+// ranking), and the two inspection kernels (proxy scores of a row range,
+// block selection mask).
 //
 // Sol-Engine LTX25 page, "Stage 2 Optimization -- Core Technology: Sol-Attn":
 // pooled keys give per-row block proxy scores whose mean and spread set the
