@@ -140,7 +140,6 @@ struct ShardPlan {
   bool moments, order;
 };
 
-
 ShardPlan make_shard_plan(int N, int Nk, int nb_all, int H, int B, bool sparse) {
   ShardPlan p{};
   p.nb = cdiv(Nk, sparse ? B : 128);
@@ -443,8 +442,9 @@ int sol_attn_tile_schedule(const uint16_t* q, const uint16_t* k, const uint16_t*
                            int* order, int N, int H, int d, int B, float beta, int Nk,
                            void* workspace, size_t ws_bytes, void* stream) {
   if (Nk == 0) Nk = N;
-  if (!work || !order) return SOL_ERR_INVALID_ARG;
+  if (!work || !order || !aligned(work, 4) || !aligned(order, 4)) return SOL_ERR_INVALID_ARG;
   if (isinf(beta) && beta < 0) return SOL_ERR_INVALID_ARG;  // dense: no selection to count
+  // the forward's checks; there is no output here, so q stands in for it
   if (int r = check_forward(q, k, v, q, N, H, d, B, beta, SOL_SPARSE, Nk)) return r;
   if (cdiv(N, 128) > kOrderMaxTiles) return SOL_ERR_UNSUPPORTED;
   const Plan p = make_plan(N, Nk, H, B, SOL_SPARSE);

@@ -196,6 +196,8 @@ int sol_attn_forward_noalloc(const uint16_t* q, const uint16_t* k, const uint16_
  * SOL_ERR_UNSUPPORTED.
  * workspace, ws_bytes: at least sol_attn_workspace_size(N, Nk, H, d, B,
  *          SOL_SPARSE) bytes, 256-byte aligned.
+ * work and order 4-byte aligned, q, k, v 16-byte aligned (SOL_ERR_INVALID_ARG
+ * otherwise).
  */
 int sol_attn_tile_schedule(const uint16_t* q, const uint16_t* k, const uint16_t* v, int* work,
                            int* order, int N, int H, int d, int B, float beta, int Nk,

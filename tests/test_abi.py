@@ -112,6 +112,8 @@ def test_other_entry_points_argument_errors(lib):
     assert ts(FAKE, FAKE, FAKE, FAKE, FAKE, 256, 1, 128, 96, 0.5, 0, FAKE, big, N) == -2   # B
     assert ts(FAKE, FAKE, FAKE, FAKE, FAKE, 256, 1, 128, 128, 0.5, 0, FAKE, 16, N) == -1   # short ws
     assert ts(FAKE, FAKE, FAKE, FAKE, FAKE, 4097 * 128, 1, 128, 128, 0.5, 0, FAKE, big, N) == -2
+    odd = ctypes.c_void_p(0x10002)  # not 4-byte aligned
+    assert ts(FAKE, FAKE, FAKE, odd, FAKE, 256, 1, 128, 128, 0.5, 0, FAKE, big, N) == -1
 
 
 def test_shard_entry_points_argument_errors(lib):
