@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsolattn.so")
-SOURCES = ["api.hip", "pool_stats.hip", "forward.hip", "forward_pp.hip", "merge.hip", "fp8_gemm.hip", "na3d.hip"]
+SOURCES = ["api.hip", "pool_stats.hip", "forward.hip", "forward_dense.hip", "merge.hip", "fp8_gemm.hip", "na3d.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -266,18 +266,7 @@ int forward_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint
     f.part_o = (float*)(ws + p.off_po);
     f.part_ml = (float*)(ws + p.off_pml);
   }
-  // Dense attention over long sequences (no key split) runs the 8-wave
-  // ping-pong kernel on 256-row tiles; sparse attention, dense short query
-  // sets and split keys the pipelined 4-wave kernel.
-  const long long pp_wgs = (long long)H * cdiv(N, 256);
-  const bool use_pp = !sparse && f.splits == 1 && pp_wgs >= kCUs;
-  if (use_pp) {
-    FwdArgs fp = f;
-    fp.total = (int)pp_wgs;
-    if (int r = hip_status(launch_forward_pp(fp, s))) return r;
-  } else {
-    if (int r = hip_status(launch_forward(f, sparse, sparse ? B : 128, s))) return r;
-  }
+  if (int r = hip_status(sparse ? launch_forward(f, B, s) : launch_forward_dense(f, s))) return r;
   if (f.splits > 1) {
     CombineArgs c{f.part_o, f.part_ml, out, lse, N, H, f.splits};
     if (int r = hip_status(launch_combine(c, s))) return r;
@@ -521,7 +510,7 @@ int sol_attn_forward_shard(const uint16_t* q, const uint16_t* k, const uint16_t*
       f.order = ta.order;
     }
   }
-  return hip_status(launch_forward(f, sparse, sparse ? B : 128, s));
+  return hip_status(sparse ? launch_forward(f, B, s) : launch_forward_dense(f, s));
 }
 
 int sol_attn_combine_partials(const float* part_o, const float* part_ml, int S, uint16_t* out,

@@ -175,8 +175,8 @@ hipError_t launch_proxy(const ProxyArgs& a, hipStream_t s);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t s);
 hipError_t launch_tile_order(const TileOrderArgs& a, hipStream_t s);
 constexpr int kOrderMaxTiles = 4096;  // query tiles per head the rank kernel holds in LDS
-hipError_t launch_forward(const FwdArgs& a, bool sparse, int B, hipStream_t s);
-hipError_t launch_forward_pp(const FwdArgs& a, hipStream_t s);  // dense only
+hipError_t launch_forward(const FwdArgs& a, int B, hipStream_t s);  // sparse
+hipError_t launch_forward_dense(const FwdArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_quantize_rows(const Fp8QuantArgs& a, hipStream_t s);

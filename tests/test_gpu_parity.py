@@ -271,13 +271,14 @@ def _growing_logits(H, N, Nk, slope, seed):
 def test_dense_reference_moves_on_every_unit():
     """Dense mode with logits rising ~0.25 nats per key up to ~370: the
     reference of the running sums is moved (and the sums rescaled) on every
-    unit, in the 4-wave kernel (short query set) and the ping-pong kernel.
+    unit, with the keys split over workgroups (short query set) and with one
+    workgroup per query tile.
 
     A handful of keys carry the mass here, so a denominator summed from the
     bf16-rounded probabilities would be off by up to 2^-9 relative in ln(l)
     (about 2e-3); the kernels sum the fp32 probabilities, and lse keeps the
     1e-3 bound of every other case."""
-    for H, N in ((2, 200), (16, 4096)):  # split keys / ping-pong kernel (256 workgroups)
+    for H, N in ((2, 200), (16, 4096)):  # split keys / one workgroup per tile (512 tiles)
         Q, K, V = _growing_logits(H, N, 1500, 0.25, seed=N)
         out, lse = sa.sol_attn_forward(dev(Q), dev(K), dev(V), mode=sa.SOL_DENSE)
         torch.cuda.synchronize()

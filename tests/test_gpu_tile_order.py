@@ -10,7 +10,9 @@
 - the order decides only when a tile runs: a four-head call that orders its
   2,048 tiles equals, bit for bit, the four single-head calls of 512 tiles,
   which run in natural order (neither splits its keys), and every output row
-  is written.
+  is written; likewise with a ragged last tile (4 heads of 65,636 rows);
+- at beta = +inf (no block selected) and beta = -1e6 (every block selected)
+  all tiles carry the same work and run in natural order.
 
 Inputs: the clustered generator (one centre per 128-row query block), seeded."""
 import numpy as np
@@ -61,9 +63,12 @@ def test_schedule_counts_and_order(H, N, B, beta):
         np.testing.assert_array_equal(o[h * n_qt:(h + 1) * n_qt], want, err_msg=f"head {h}")
 
 
-@pytest.mark.parametrize("B,beta", [(128, 0.5), (64, 1.0)])
-def test_ordered_call_equals_natural_order_calls(B, beta):
-    H, N = 4, 65536  # 4 x 512 tiles: the call orders; one head: 512 tiles, no split
+@pytest.mark.parametrize("H,N,B,beta", [(4, 65536, 128, 0.5), (4, 65536, 64, 1.0),
+                                        (4, 65636, 128, 0.5)])
+def test_ordered_call_equals_natural_order_calls(H, N, B, beta):
+    # 4 x 512 tiles, or 4 x 513 with a ragged last tile of 100 rows: the call
+    # orders its tiles; one head alone has too few tiles to order, and enough
+    # not to split its keys (512 workgroups or more)
     q, k, v = _inputs(H, N, seed=47, B=B)
     out = torch.full_like(q, float("nan"))
     lse = torch.full((H, N), float("nan"), dtype=torch.float32, device="cuda")
@@ -71,7 +76,7 @@ def test_ordered_call_equals_natural_order_calls(B, beta):
     work, order = sa.sol_attn_tile_schedule(q, k, v, B=B, beta=beta)
     torch.cuda.synchronize()
     assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any(), "a row was not written"
-    n_qt = N // 128
+    n_qt = (N + 127) // 128
     o = order.cpu().numpy()
     assert not np.array_equal(o, np.arange(H * n_qt)), "the call should run its tiles out of natural order"
     for h in range(H):
@@ -80,6 +85,28 @@ def test_ordered_call_equals_natural_order_calls(B, beta):
         torch.cuda.synchronize()
         assert torch.equal(oh[0], out[h]), f"head {h}: output differs from the single-head call"
         assert torch.equal(lh[0], lse[h]), f"head {h}: lse differs from the single-head call"
+
+
+@pytest.mark.parametrize("beta,count", [(float("inf"), "none"), (-1e6, "all")])
+def test_degenerate_beta_counts_and_natural_order(beta, count):
+    """beta = +inf selects no block (Taylor terms only) and beta = -1e6 every block:
+    every tile then carries the same work (0 or all blocks, the ragged last
+    block included), the order is the natural one, and the ordered call still
+    equals the single-head calls bit for bit."""
+    H, N, B = 4, 65536, 128
+    q, k, v = _inputs(H, N, seed=59, B=B)
+    work, order = sa.sol_attn_tile_schedule(q, k, v, B=B, beta=beta)
+    out, lse = sa.sol_attn_forward(q, k, v, B=B, beta=beta)
+    torch.cuda.synchronize()
+    n_qt, nb = N // 128, N // B
+    want = 0 if count == "none" else nb
+    assert (work.cpu().numpy() == want).all(), f"work counts should all be {want}"
+    np.testing.assert_array_equal(order.cpu().numpy(), np.arange(H * n_qt))
+    for h in (0, H - 1):
+        oh, lh = sa.sol_attn_forward(q[h:h + 1].contiguous(), k[h:h + 1].contiguous(),
+                                     v[h:h + 1].contiguous(), B=B, beta=beta)
+        torch.cuda.synchronize()
+        assert torch.equal(oh[0], out[h]) and torch.equal(lh[0], lse[h]), f"head {h}"
 
 
 def test_schedule_argument_errors():
