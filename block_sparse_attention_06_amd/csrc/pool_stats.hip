@@ -353,7 +353,7 @@ hipError_t launch_moments(const MomentArgs& a, hipStream_t s) {
 }
 
 // stats_moment_kernel: one wave per 32 query rows, four per 128-row tile, and
-// kMomentTiles consecutive tiles per workgroup.  Y^T = C Q^T runs on MFMA over
+// a contiguous range of tiles per workgroup.  Y^T = C Q^T runs on MFMA over
 // the stored block-triangular C: row tile ct takes the k-steps of column
 // blocks ct .. 3 only (20 of 32 k-steps, x (hi, lo)); each lane dots the
 // accumulator elements of a row tile with the matching query values, which it
@@ -361,12 +361,17 @@ hipError_t launch_moments(const MomentArgs& a, hipStream_t s) {
 // takes two query tiles per pass, so each C operand read from LDS feeds two
 // products.
 //
+// The grid is fixed at about three workgroups per CU (kMomentWGs over the
+// heads): workgroup x of head h takes the contiguous tile range
+// [x nt / G, (x + 1) nt / G) of that head, so C is staged once per workgroup
+// and no last round of workgroups runs the chip part-empty.
+//
 // Only the used blocks of C are staged, once per workgroup: row R of tile ct
 // keeps 16-byte chunks 4 ct .. 15, at positions 0 .. 15 - 4 ct of a row of
 // kCW[ct] chunks (an odd count, so that 8 consecutive rows start on different
 // banks: conflict-free operand reads).  45 KiB per workgroup; three
 // workgroups per CU hide the query loads (there is no register prefetch).
-constexpr int kMomentTiles = 8;
+constexpr int kMomentWGs = 3 * 256;  // resident workgroups: three per CU
 constexpr int kCW0 = 17, kCW1 = 13, kCW2 = 9, kCW3 = 5;   // padded row widths (chunks)
 constexpr int kCBase1 = 32 * kCW0, kCBase2 = kCBase1 + 32 * kCW1, kCBase3 = kCBase2 + 32 * kCW2;
 constexpr int kCChunks = kCBase3 + 32 * kCW3;             // 1408 chunks per part
@@ -406,21 +411,27 @@ __global__ __launch_bounds__(256, 3) void stats_moment_kernel(StatsMomentArgs a)
   }
   if (tid < kHeadDim) mb[tid] = a.mbar[(int64_t)h * kHeadDim + tid];
   const u16* qh = a.q + (int64_t)h * a.N * kHeadDim;
-  const int row0 = blockIdx.x * kMomentTiles * kQTile + wave * 32 + (lane & 31);
+  const int nt = (a.N + kQTile - 1) / kQTile;
+  const int t_begin = (int)((int64_t)blockIdx.x * nt / gridDim.x);
+  const int t_end = (int)((int64_t)(blockIdx.x + 1) * nt / gridDim.x);
   __syncthreads();
   const int r = lane & 31;
   const float scale = 0.08838834764831845f;  // 1/sqrt(128)
-  for (int t = 0; t < kMomentTiles; t += 2) {
-    const int rowa = row0 + t * kQTile, rowb = rowa + kQTile;
-    if (rowa - r >= a.N) break;  // wave-uniform: the wave's first row is past the end
+  for (int t = t_begin; t < t_end; t += 2) {
+    const int rowa = t * kQTile + wave * 32 + r, rowb = rowa + kQTile;
+    const bool va = rowa < a.N, vb = t + 1 < t_end && rowb < a.N;
     QFrag qa, qb;
-    load_qfrag(qa, qh, rowa, rowa < a.N, g);
-    load_qfrag(qb, qh, rowb, rowb < a.N, g);
+    load_qfrag(qa, qh, rowa, va, g);
+    load_qfrag(qb, qh, rowb, vb, g);
     float s2a = 0.f, s2b = 0.f, s1a = 0.f, s1b = 0.f;
+    // an opaque zero: keeps the C operand reads inside the loop (hoisted, the
+    // 40 operands of a pass would not fit the register budget)
+    int cz = 0;
+    asm volatile("" : "+v"(cz));
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       f32x16 ya = {}, yb = {};
-      const int rbase = (c_base(ct) + r * c_width(ct) - 4 * ct) * 8;
+      const int rbase = (c_base(ct) + r * c_width(ct) - 4 * ct) * 8 + cz;
 #pragma unroll
       for (int ks = 2 * ct; ks < 8; ++ks) {
         const int off = rbase + (ks * 2 + g) * 8;
@@ -436,7 +447,7 @@ __global__ __launch_bounds__(256, 3) void stats_moment_kernel(StatsMomentArgs a)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int ks = 2 * ct + (e >> 3), k = e & 7;
-        const float m = mb[16 * ks + 8 * g + k];
+        const float m = mb[16 * ks + 8 * g + k + cz];
         const float xa = (float)qa.k[ks][k], xb = (float)qb.k[ks][k];
         s2a = __builtin_fmaf(ya[e], xa, s2a);
         s2b = __builtin_fmaf(yb[e], xb, s2b);
@@ -448,11 +459,11 @@ __global__ __launch_bounds__(256, 3) void stats_moment_kernel(StatsMomentArgs a)
     s2a += __shfl_xor(s2a, 32);
     s1b += __shfl_xor(s1b, 32);
     s2b += __shfl_xor(s2b, 32);
-    if (g == 0 && rowa < a.N) {
+    if (g == 0 && va) {
       a.mu[(int64_t)h * a.N + rowa] = s1a * scale;
       a.sigma[(int64_t)h * a.N + rowa] = sqrtf(fmaxf(s2a, 0.f)) * scale;
     }
-    if (g == 0 && rowb < a.N) {
+    if (g == 0 && vb) {
       a.mu[(int64_t)h * a.N + rowb] = s1b * scale;
       a.sigma[(int64_t)h * a.N + rowb] = sqrtf(fmaxf(s2b, 0.f)) * scale;
     }
@@ -460,7 +471,11 @@ __global__ __launch_bounds__(256, 3) void stats_moment_kernel(StatsMomentArgs a)
 }
 
 hipError_t launch_stats_moment(const StatsMomentArgs& a, hipStream_t s) {
-  dim3 grid((a.N + kMomentTiles * kQTile - 1) / (kMomentTiles * kQTile), a.H);
+  // workgroups per head: kMomentWGs shared over the heads, at most one per
+  // two tiles and at least one
+  const int nt = (a.N + kQTile - 1) / kQTile;
+  const int per_head = std::max(1, std::min((nt + 1) / 2, kMomentWGs / std::max(1, a.H)));
+  dim3 grid(per_head, a.H);
   return launch_kernel(stats_moment_kernel, grid, dim3(256), s, a);
 }
 
