@@ -209,6 +209,20 @@ __device__ __forceinline__ uint32_t partner_b(uint32_t x, int g) {
   return g ? r[0] : r[1];
 }
 
+// OR of a 32-bit value over the 64 lanes of a wave (every lane active), as a
+// wave-uniform value: shifts within each row of 16 lanes leave the row's OR in
+// its lane 15, two row broadcasts carry rows 0-1 into lane 31 and all four
+// rows into lane 63, which is read out.  Lanes without a source take 0.
+__device__ __forceinline__ uint32_t wave_or(uint32_t x) {
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 // Sum and maximum over the lane pair (l, l ^ 32); the same value in both lanes.
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

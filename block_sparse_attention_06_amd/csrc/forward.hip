@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             const int c0 = c_next;
             const f32x16 p = proxy_chunk_hl(qf, khi, klo, c0, lane);
             const float f = fast_exp2(mu * kLog2e - m);  // e^{mu} relative to the reference
-            uint32_t sel_bits = 0, wsel = 0;  // this row's, and the wave's (scalar)
+            uint32_t sel_bits = 0;  // this row's selections
             // Weights enter the MFMA as bf16 hi + lo parts: when many blocks
             // share nearly the same weight, a single bf16 rounding would bias
             // the Taylor mass coherently instead of averaging out.
@@ -372,10 +372,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
               const bool inr = qvalid && g4 < t_end - c0 - ci;
               const bool sel = inr && is_selected(p[i], tau);
               sel_bits |= (uint32_t)sel << ci;
-              // lanes 0-31 hold block ci of their rows, lanes 32-63 block ci + 4
-              const uint64_t bal = __builtin_amdgcn_ballot_w64(sel);
-              wsel |= ((uint32_t)bal != 0u ? 1u : 0u) << ci;
-              wsel |= ((uint32_t)(bal >> 32) != 0u ? 1u : 0u) << (ci + 4);
               const float wt = (inr && !sel) ? (1.f + p[i] - mu) * f : 0.f;
               __bf16 wh, wl;
               split_bf16(wt, wh, wl);
@@ -400,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             }
             l += wden;
             fullA = sel_bits | partner_b(sel_bits, g);
-            const uint32_t w = wsel;
+            const uint32_t w = wave_or(sel_bits);  // the wave's selections
             wvA = w;
             // Exchange the wave masks through the last bytes of the K tile of
             // the stage about to be refilled: nothing reads that stage until

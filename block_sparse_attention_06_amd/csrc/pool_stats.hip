@@ -556,16 +556,14 @@ __global__ __launch_bounds__(512) void tile_work_kernel(TileOrderArgs a) {
     }
     const float scale = 0.08838834764831845f;  // 1/sqrt(128)
     const int b0 = c * kChunk;
-    // the wave's union per block from one ballot per accumulator element: lanes
-    // 0-31 hold block acc_row(i, 0) of their rows, lanes 32-63 block acc_row(i, 1)
-    // (invalid rows have tau = +inf and select nothing)
-    uint32_t mine = 0;
+    // the wave's union per block: each lane's selections as a bit mask (element
+    // i is block acc_row(i, 0) + 4g; invalid rows have tau = +inf and select
+    // nothing), OR-ed over the wave
+    uint32_t bits = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint64_t b = __builtin_amdgcn_ballot_w64(is_selected(acc[i] * scale, tau));
-      mine |= ((uint32_t)b != 0u ? 1u : 0u) << acc_row(i, 0);
-      mine |= ((uint32_t)(b >> 32) != 0u ? 1u : 0u) << acc_row(i, 1);
-    }
+    for (int i = 0; i < 16; ++i)
+      bits |= is_selected(acc[i] * scale, tau) ? 1u << acc_row(i, 0) : 0u;
+    uint32_t mine = wave_or(bits << (4 * g));
     const int left = a.nb - b0;  // blocks of this chunk that exist
     if (left < 32) mine &= (1u << left) - 1u;
     if (lane == 0) wmask[c & 1][wave] = mine;
