@@ -505,7 +505,7 @@ hipError_t launch_stats_moment(const StatsMomentArgs& a, hipStream_t s) {
 // union a lane of waves 0 and 4 then counts.
 constexpr int kWorkStages = 3;
 constexpr int kWorkStageBytes = kChunk * kHeadDim * 2;  // 8 KiB
-constexpr int kWorkWaitOne = 0x0F71;                    // s_waitcnt vmcnt(1)
+constexpr int kWorkWaitOne = 0x0071;  // s_waitcnt vmcnt(1) lgkmcnt(0): also the wave-mask write
 
 __global__ __launch_bounds__(512) void tile_work_kernel(TileOrderArgs a) {
   __shared__ __attribute__((aligned(16))) u16 stage[kWorkStages][kWorkStageBytes / 2];
@@ -539,7 +539,7 @@ __global__ __launch_bounds__(512) void tile_work_kernel(TileOrderArgs a) {
   const bool counter = lane == 0 && (wave & 3) == 0;  // lane 0 of waves 0 and 4
   const int tbase = wave & 4;
   for (int c = 0; c < n_chunks; ++c) {
-    __builtin_amdgcn_s_waitcnt(kWorkWaitOne);  // this wave's load of chunk c landed
+    __builtin_amdgcn_s_waitcnt(kWorkWaitOne);  // this wave's load of chunk c and its mask write landed
     __builtin_amdgcn_s_barrier();              // every wave's; stage of c - 1 read
     asm volatile("" ::: "memory");
     dma_chunk(c + 2, (c + 2) % kWorkStages);
