@@ -7,20 +7,29 @@
 // range is split over workgroups and the partial answers, each carrying its
 // running maximum and denominator, are merged exactly (combine_kernel).
 //
-// Workgroup: 4 waves x 32 query rows = 128 rows of one head, and three
-// workgroups per CU (at most 168 registers per lane, 48 KiB of LDS each), so
-// every SIMD holds three waves: while one runs its softmax on the vector unit,
-// another issues matrix products.  Keys stream through LDS in units of 32 rows
-// of K and V, in a ring of three stages filled by direct global->LDS loads.
-// Iteration i issues the loads of unit i + 2 into the stage unit i - 1 left
-// (free since the barrier that ended iteration i - 1), then computes
-// S^T = K Q^T of unit i, its online softmax and O^T += V^T P^T, and waits
-// for its own loads of unit i + 1; one barrier per unit publishes them.
+// Each wave owns 32 query rows, and every SIMD holds three waves: while one
+// runs its softmax on the vector unit, another issues matrix products (at most
+// 168 registers per lane).  Keys stream through LDS in units of 32 rows of K
+// and V, filled by direct global->LDS loads from waves 0-3.  Two forms:
+//
+//  - W = 4: 128 query rows per workgroup, three workgroups per CU (48 KiB of
+//    LDS each), a ring of three stages, one unit per iteration: iteration i
+//    issues the loads of unit i + 2 into the stage unit i - 1 left (free since
+//    the barrier that ended iteration i - 1), then computes S^T = K Q^T of
+//    unit i, its online softmax and O^T += V^T P^T, and waits for its own
+//    loads of unit i + 1; one barrier per unit publishes them.  Short query
+//    sets (key splits) and small calls use it.
+//  - W = 12: 384 query rows per workgroup, one workgroup per CU (96 KiB), a
+//    ring of six stages, two units per iteration and barrier, loads four units
+//    ahead.  Each staged unit feeds twelve waves instead of four, so a third
+//    of the L2->LDS traffic of the W = 4 form crosses the chip for the same
+//    products; on this power-limited part that buys clock (4K dense 0.7-2 %
+//    faster on two boxes).  Long sequences use it.
 //
 // Against a pipelined loop at two workgroups per CU (each wave overlapping the
 // softmax of one unit with the products of the next) and an 8-wave ping-pong
 // schedule, the third wave per SIMD does the overlapping instead: 4K dense
-// 234.8 vs 248.2 ms on one box, stage-2 8.97 vs 9.77 ms.
+// 234.8 vs 248.2 ms on one box, stage-2 8.97 vs 9.77 ms (W = 4 form).
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -30,18 +39,29 @@ namespace {
 
 constexpr int kDU = 32;                  // keys per staged unit
 constexpr int kDUE = kDU * kHeadDim;     // bf16 per tensor per stage
-constexpr int kDRing = 3;                // LDS stages (48 KiB: three workgroups per CU)
 constexpr int kDTile = 128;              // keys per split tile
 // The running sums' reference may lag a row's maximum by up to 8 (log2
 // units): a lane's row sum of one unit's probabilities stays within 2^8.
 constexpr float kDSlackSum = 256.f;
-// s_waitcnt vmcnt(4): at the end of iteration i this wave's four loads of
-// unit i + 1 have landed; the four of unit i + 2 may still be in flight.
-constexpr int kDWaitNext = 0x0F74;
+// Workgroups of the W = 12 form that fill the chip once (one per CU).
+constexpr int kDWideMinWGs = 256;
+
+// Per form: units per iteration P, ring stages 3P, and the wait at the end of
+// an iteration: a loading wave issues 4 loads per unit, so vmcnt(4P) leaves
+// the P units issued in this iteration in flight and has the next P landed.
+template <int W> struct DenseForm {
+  static constexpr int P = W == 4 ? 1 : 2;
+  static constexpr int kRing = 3 * P;
+  static constexpr int kWait = 0x0F70 | (4 * P);  // s_waitcnt vmcnt(4P)
+  static constexpr int kRows = 32 * W;
+};
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 3) void fwd_dense_kernel(FwdArgs a) {
+template <int W>
+__global__ __launch_bounds__(64 * W, W == 4 ? 3 : 1) void fwd_dense_kernel(FwdArgs a) {
+  using F = DenseForm<W>;
+  constexpr int kDRing = F::kRing;
   __shared__ __attribute__((aligned(16))) u16 lds_k[kDRing][kDUE];
   __shared__ __attribute__((aligned(16))) u16 lds_v[kDRing][kDUE];
 
@@ -56,7 +76,7 @@ __global__ __launch_bounds__(256, 3) void fwd_dense_kernel(FwdArgs a) {
   const int split = logical % a.splits;
   const int tq = logical / a.splits;
   const int qt = tq % a.n_qt, h = tq / a.n_qt;
-  const int row = qt * kQTile + wave * 32 + r32;
+  const int row = qt * F::kRows + wave * 32 + r32;
   const bool qvalid = row < a.N;
 
   QFrag qf;
@@ -76,7 +96,7 @@ __global__ __launch_bounds__(256, 3) void fwd_dense_kernel(FwdArgs a) {
   // that no wait it places later also waits for the key/value loads below.
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- direct loads of one unit: wave w fills K and V rows 8w .. 8w+7 in two
+  // ---- direct loads of one unit (waves 0-3): wave w fills K and V rows 8w .. 8w+7 in two
   // groups of four rows (1 KiB per instruction); lane l lands in chunk slot
   // l % 16 of row l / 16 of its group and fetches the global chunk that slot
   // holds.  Offsets are relative to the unit's first key.
@@ -229,17 +249,13 @@ __global__ __launch_bounds__(256, 3) void fwd_dense_kernel(FwdArgs a) {
     const bool have = u_next < u_end;
     const int key0 = have ? u_next * kDU : 0;
     if (have) ++u_next;
-    dma_unit(key0, st);
+    if (W == 4 || wave < 4) dma_unit(key0, st);
     skey[st] = key0;
     sval = have ? (sval | (1u << st)) : (sval & ~(1u << st));
   };
 
-  // One iteration for the unit in stage st.  Returns false once the stream
-  // is exhausted and no issued unit is left.
-  auto iteration = [&](const int st) __attribute__((always_inline)) -> bool {
-    const int st_next = st == kDRing - 1 ? 0 : st + 1;
-    const int st_new = st_next == kDRing - 1 ? 0 : st_next + 1;
-    issue_next(st_new);
+  // The unit in stage st, if it holds one.
+  auto compute = [&](const int st) __attribute__((always_inline)) {
     if ((sval >> st) & 1u) {
       f32x16 s = mma_s(st);
       mask_ragged(s, skey[st]);
@@ -252,20 +268,32 @@ __global__ __launch_bounds__(256, 3) void fwd_dense_kernel(FwdArgs a) {
       l += rsum;
       mma_pv(st, pb);
     }
-    __builtin_amdgcn_s_waitcnt(kDWaitNext);  // this wave's loads of the next unit landed
-    wg_barrier();                            // ... and every wave's; stage st is free
-    return !(u_next >= u_end && ((sval >> st_next) & 1u) == 0 && ((sval >> st_new) & 1u) == 0);
+  };
+  // One iteration for the P units in stages st .. st + P - 1: the units 2P
+  // ahead are issued into the stages the previous iteration computed (free
+  // since the barrier that ended it).  Returns false once the stream is
+  // exhausted and no issued unit is left.
+  auto iteration = [&](const int st) __attribute__((always_inline)) -> bool {
+#pragma unroll
+    for (int j = 0; j < F::P; ++j) issue_next((st + 2 * F::P + j) % kDRing);
+#pragma unroll
+    for (int j = 0; j < F::P; ++j) compute(st + j);
+    __builtin_amdgcn_s_waitcnt(F::kWait);  // this wave's loads of the next P units landed
+    wg_barrier();                          // ... and every wave's
+    bool left = u_next < u_end;
+#pragma unroll
+    for (int j = F::P; j < kDRing; ++j) left = left || ((sval >> ((st + j) % kDRing)) & 1u) != 0;
+    return left;
   };
 
-  // prologue: units 0 and 1 into stages 0 and 1
-  issue_next(0);
-  issue_next(1);
-  __builtin_amdgcn_s_waitcnt(kDWaitNext);
+  // prologue: units 0 .. 2P - 1 into the first 2P stages
+#pragma unroll
+  for (int j = 0; j < 2 * F::P; ++j) issue_next(j);
+  __builtin_amdgcn_s_waitcnt(F::kWait);
   wg_barrier();
   // the loop is unrolled over one turn of the ring, so that every stage index
   // (and with it every LDS offset and load destination) is a constant
-  static_assert(kDRing == 3, "the loop below is one turn of a three-stage ring");
-  while (iteration(0) && iteration(1) && iteration(2)) {
+  while (iteration(0) && iteration(F::P) && iteration(2 * F::P)) {
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load may land after the workgroup ends
 
@@ -307,8 +335,17 @@ __global__ __launch_bounds__(256, 3) void fwd_dense_kernel(FwdArgs a) {
 }
 
 hipError_t launch_forward_dense(const FwdArgs& a, hipStream_t s) {
+  // Without a key split and with enough 384-row tiles to fill the chip, the
+  // W = 12 form; otherwise the W = 4 form on the 128-row tiles of the plan.
+  const int n_wide = (a.N + DenseForm<12>::kRows - 1) / DenseForm<12>::kRows;
+  if (a.splits == 1 && (long long)a.H * n_wide >= kDWideMinWGs) {
+    FwdArgs w = a;
+    w.n_qt = n_wide;
+    w.total = a.H * n_wide;
+    return launch_kernel(fwd_dense_kernel<12>, dim3((w.total + 7) & ~7), dim3(768), s, w);
+  }
   const int grid = (a.total + 7) & ~7;
-  return launch_kernel(fwd_dense_kernel, dim3(grid), dim3(256), s, a);
+  return launch_kernel(fwd_dense_kernel<4>, dim3(grid), dim3(256), s, a);
 }
 
 }  // namespace solattn
