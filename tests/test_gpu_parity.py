@@ -271,18 +271,21 @@ def _growing_logits(H, N, Nk, slope, seed):
 def test_dense_reference_moves_on_every_unit():
     """Dense mode with logits rising ~0.25 nats per key up to ~370: the
     reference of the running sums is moved (and the sums rescaled) on every
-    unit, with the keys split over workgroups (short query set) and with one
-    workgroup per query tile.
+    unit, with the keys split over workgroups (short query set), with one
+    4-wave workgroup per 128-row query tile, and with the 12-wave form on
+    384-row tiles (32 heads x 11 tiles: its last tile holds 100 rows, so waves
+    4-11 hold none and wave 3 four; the last 32-key unit is ragged).
 
     A handful of keys carry the mass here, so a denominator summed from the
     bf16-rounded probabilities would be off by up to 2^-9 relative in ln(l)
     (about 2e-3); the kernels sum the fp32 probabilities, and lse keeps the
     1e-3 bound of every other case."""
-    for H, N in ((2, 200), (16, 4096)):  # split keys / one workgroup per tile (512 tiles)
+    # split keys / 4-wave tiles (512) / 12-wave tiles (352, ragged last tile)
+    for H, N in ((2, 200), (16, 4096), (32, 3940)):
         Q, K, V = _growing_logits(H, N, 1500, 0.25, seed=N)
         out, lse = sa.sol_attn_forward(dev(Q), dev(K), dev(V), mode=sa.SOL_DENSE)
         torch.cuda.synchronize()
-        rows = np.arange(0, N, max(1, N // 200))
+        rows = np.union1d(np.arange(0, N, max(1, N // 200)), np.arange(max(0, N - 130), N))
         for h in (0, H - 1):
             o, l = O.dense_head_ref(_head(Q, h), _head(K, h), _head(V, h), rows=rows)
             check_close(host(out[h])[rows], o, host(lse[h])[rows], l, what=f"dense growing N{N} h{h}")
