@@ -10,7 +10,7 @@
 // Each wave owns 32 query rows, and every SIMD holds three waves: while one
 // runs its softmax on the vector unit, another issues matrix products (at most
 // 168 registers per lane).  Keys stream through LDS in units of 32 rows of K
-// and V, filled by direct global->LDS loads from waves 0-3.  Two forms:
+// and V, each unit filled by direct global->LDS loads from four waves.  Two forms:
 //
 //  - W = 4: 128 query rows per workgroup, three workgroups per CU (48 KiB of
 //    LDS each), a ring of three stages, one unit per iteration: iteration i
@@ -21,7 +21,7 @@
 //    sets (key splits) and small calls use it.
 //  - W = 12: 384 query rows per workgroup, one workgroup per CU (96 KiB), a
 //    ring of six stages, two units per iteration and barrier, loads four units
-//    ahead.  Each staged unit feeds twelve waves instead of four, so a third
+//    ahead, the two units of a pair loaded by waves 0-3 and 4-7.  Each staged unit feeds twelve waves instead of four, so a third
 //    of the L2->LDS traffic of the W = 4 form crosses the chip for the same
 //    products; on this power-limited part that buys clock (4K dense 0.7-2 %
 //    faster on two boxes).  Long sequences use it.
@@ -46,13 +46,15 @@ constexpr float kDSlackSum = 256.f;
 // Workgroups of the W = 12 form that fill the chip once (one per CU).
 constexpr int kDWideMinWGs = 256;
 
-// Per form: units per iteration P, ring stages 3P, and the wait at the end of
-// an iteration: a loading wave issues 4 loads per unit, so vmcnt(4P) leaves
-// the P units issued in this iteration in flight and has the next P landed.
+// Per form: units per iteration P and ring stages 3P.  A loading wave issues
+// the 4 loads of one unit per iteration (W = 4: every wave, its quarter of the
+// unit; W = 12: waves 0-3 the first unit of the pair, waves 4-7 the second),
+// so vmcnt(4) at the end of an iteration leaves this iteration's unit in
+// flight and has the one issued an iteration earlier landed.
 template <int W> struct DenseForm {
   static constexpr int P = W == 4 ? 1 : 2;
   static constexpr int kRing = 3 * P;
-  static constexpr int kWait = 0x0F70 | (4 * P);  // s_waitcnt vmcnt(4P)
+  static constexpr int kWait = 0x0F74;  // s_waitcnt vmcnt(4)
   static constexpr int kRows = 32 * W;
 };
 
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 3 : 1) void fwd_dense_kernel(FwdAr
   // that no wait it places later also waits for the key/value loads below.
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- direct loads of one unit (waves 0-3): wave w fills K and V rows 8w .. 8w+7 in two
+  // ---- direct loads of one unit (four waves): wave w fills K and V rows 8(w % 4) .. +7 in two
   // groups of four rows (1 KiB per instruction); lane l lands in chunk slot
   // l % 16 of row l / 16 of its group and fetches the global chunk that slot
   // holds.  Offsets are relative to the unit's first key.
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 3 : 1) void fwd_dense_kernel(FwdAr
   uint32_t offk[2], offv[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int r = wave * 8 + i * 4 + (lane >> 4);
+    const int r = (wave & 3) * 8 + i * 4 + (lane >> 4);
     offk[i] = (uint32_t)(r * kHeadDim + (kslot(r, slot) << 3)) * 2u;
     offv[i] = (uint32_t)(r * kHeadDim + (vslot(r, slot) << 3)) * 2u;
   }
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 3 : 1) void fwd_dense_kernel(FwdAr
     if (key0 + kDU <= Nk) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int r0 = wave * 8 + i * 4;
+        const int r0 = (wave & 3) * 8 + i * 4;
         dma16_sv(kb, offk[i], lds_addr(&lds_k[st][r0 * kHeadDim]));
         dma16_sv(vb, offv[i], lds_addr(&lds_v[st][r0 * kHeadDim]));
       }
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 3 : 1) void fwd_dense_kernel(FwdAr
       // data); their scores are masked and their probabilities are zero
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int r0 = wave * 8 + i * 4;
+        const int r0 = (wave & 3) * 8 + i * 4;
         const int r = r0 + (lane >> 4);
         const int rr = min(r, Nk - 1 - key0);
         const uint32_t ok = (uint32_t)(rr * kHeadDim + (kslot(r, slot) << 3)) * 2u;
@@ -245,11 +247,11 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 3 : 1) void fwd_dense_kernel(FwdAr
   // Issues the next unit of the stream into stage st (a stream past its end
   // reloads key 0 into a stage nobody reads, so the count of loads in flight
   // stays exact).
-  auto issue_next = [&](const int st) __attribute__((always_inline)) {
+  auto issue_next = [&](const int st, const int grp) __attribute__((always_inline)) {
     const bool have = u_next < u_end;
     const int key0 = have ? u_next * kDU : 0;
     if (have) ++u_next;
-    if (W == 4 || wave < 4) dma_unit(key0, st);
+    if (W == 4 || (wave >> 2) == grp) dma_unit(key0, st);
     skey[st] = key0;
     sval = have ? (sval | (1u << st)) : (sval & ~(1u << st));
   };
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 3 : 1) void fwd_dense_kernel(FwdAr
   // exhausted and no issued unit is left.
   auto iteration = [&](const int st) __attribute__((always_inline)) -> bool {
 #pragma unroll
-    for (int j = 0; j < F::P; ++j) issue_next((st + 2 * F::P + j) % kDRing);
+    for (int j = 0; j < F::P; ++j) issue_next((st + 2 * F::P + j) % kDRing, j);
 #pragma unroll
     for (int j = 0; j < F::P; ++j) compute(st + j);
     __builtin_amdgcn_s_waitcnt(F::kWait);  // this wave's loads of the next P units landed
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 3 : 1) void fwd_dense_kernel(FwdAr
 
   // prologue: units 0 .. 2P - 1 into the first 2P stages
 #pragma unroll
-  for (int j = 0; j < 2 * F::P; ++j) issue_next(j);
+  for (int j = 0; j < 2 * F::P; ++j) issue_next(j, j % F::P);
   __builtin_amdgcn_s_waitcnt(F::kWait);
   wg_barrier();
   // the loop is unrolled over one turn of the ring, so that every stage index
